@@ -1,0 +1,414 @@
+/*
+ * CPU oracle for the gpt-oss-style Mixture-of-Experts FFN layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the slow, obviously-correct
+ * definition the HIP library is checked against.  Only the tests, the smoke
+ * check and the CPU-baseline leg of the benchmark may load it; the product
+ * path never does.  It shares no code, header, table or constant with the
+ * HIP library.
+ *
+ * Every value is taken as the exact real number its bits encode and all
+ * arithmetic is IEEE double in plain loop order, with no blocking, fusion or
+ * intermediate rounding.
+ *
+ * What the layer computes, with sources:
+ *  - top-4-of-32 (120b: of 128) expert routing per token and SwiGLU experts:
+ *    "Persona Kappa: training a 20B LLM on desktop GPUs" (Level1Techs),
+ *    table "Architecture Summary"; "hearth-lean-loomed-v1" model card,
+ *    section "Why 12-16 streams can be slow on Vulkan".
+ *  - expert weights natively MXFP4, activations kept in bf16 (W4A16):
+ *    Persona Kappa post, section "Quantization-Aware Training (QAT)";
+ *    "gpt-oss-20b" model page (coolboxapp), section "Architecture".
+ *  The pages give no formulas.  The readings taken where they are silent:
+ *    routing  = top-k by logit, ties to the lower expert index, slots in
+ *               descending-logit order, softmax over the k selected;
+ *    SwiGLU   = silu(gate) * up, silu(z) = z / (1 + exp(-z)), no bias/clamp;
+ *    layouts  = weights stored [out][in] (K contiguous); the fused gate/up
+ *               matrix has the I gate rows first, then the I up rows;
+ *    MXFP4    = OCP Microscaling v1.0: E2M1 elements, one E8M0 scale per 32
+ *               consecutive elements along K, element 2b in the low nibble
+ *               of byte b and element 2b+1 in the high nibble;
+ *    permute  = stable counting sort of pair ids p = t*k + j by expert.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORC_OK 0
+#define ORC_ERR_ARG 1
+#define ORC_ERR_NOMEM 2
+
+/* Planted-mistake switch: the oracle's self-tests rebuild this file with
+ * -DORC_PLANT=n to check that each pin catches a plausible mistake.  The
+ * default build plants nothing. */
+#ifndef ORC_PLANT
+#define ORC_PLANT 0
+#endif
+
+/* ---------------------------------------------------------------- decode */
+
+/* bf16 is the upper half of an IEEE binary32; widening is exact. */
+double orc_bf16_value(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* E2M1 (OCP MX v1.0): sign bit 3, exponent bits 2:1 (bias 1), mantissa
+ * bit 0.  Exponent field 0 is subnormal: 0.m * 2^0 = m/2. */
+double orc_e2m1_value(unsigned code)
+{
+    unsigned s = (code >> 3) & 1u, e = (code >> 1) & 3u, m = code & 1u;
+    double mag = (e == 0) ? 0.5 * (double)m : ldexp(1.0 + 0.5 * (double)m, (int)e - 1);
+    return s ? -mag : mag;
+}
+
+/* E8M0 scale: 2^(S-127); S = 255 encodes NaN. */
+double orc_e8m0_value(unsigned s)
+{
+    if (s == 255u) return NAN;
+    return ldexp(1.0, (int)s - 127);
+}
+
+/* Element c of an MXFP4 row: nibble c%2 of byte c/2, scaled by block c/32. */
+double orc_mxfp4_value(const uint8_t* row_bytes, const uint8_t* row_scales, int64_t c)
+{
+    uint8_t b = row_bytes[c / 2];
+#if ORC_PLANT == 5
+    unsigned code = (c & 1) ? (b & 15u) : (b >> 4); /* planted: nibble order swapped */
+#else
+    unsigned code = (c & 1) ? (b >> 4) : (b & 15u);
+#endif
+    return orc_e2m1_value(code) * orc_e8m0_value(row_scales[c / 32]);
+}
+
+/* Decode matrix `expert` of a batched weight tensor [E][rows][cols] into
+ * doubles.  wfmt 0: bf16 elements; wfmt 1: MXFP4 bytes [E][rows][cols/2] plus
+ * scales [E][rows][cols/32]. */
+static void decode_expert_matrix(int wfmt, const void* data, const uint8_t* scales,
+                                 int64_t rows, int64_t cols, int64_t expert, double* out)
+{
+    for (int64_t r = 0; r < rows; ++r) {
+        if (wfmt == 0) {
+            const uint16_t* src = (const uint16_t*)data + (expert * rows + r) * cols;
+            for (int64_t c = 0; c < cols; ++c) out[r * cols + c] = orc_bf16_value(src[c]);
+        } else {
+            const uint8_t* rb = (const uint8_t*)data + (expert * rows + r) * (cols / 2);
+            const uint8_t* rs = scales + (expert * rows + r) * (cols / 32);
+            for (int64_t c = 0; c < cols; ++c) out[r * cols + c] = orc_mxfp4_value(rb, rs, c);
+        }
+    }
+}
+
+int orc_decode_expert_matrix(int wfmt, const void* data, const uint8_t* scales,
+                             int64_t rows, int64_t cols, int64_t expert, double* out)
+{
+    if (!data || !out || rows < 0 || cols < 0 || expert < 0) return ORC_ERR_ARG;
+    if (wfmt == 1 && (!scales || cols % 32 != 0)) return ORC_ERR_ARG;
+    if (wfmt != 0 && wfmt != 1) return ORC_ERR_ARG;
+    decode_expert_matrix(wfmt, data, scales, rows, cols, expert, out);
+    return ORC_OK;
+}
+
+/* ---------------------------------------------------------------- routing */
+
+/* Router logit l[e] = sum_h x[h] * Wr[e][h], summed in h order. */
+static void router_logits_one(int H, int E, const uint16_t* xrow, const uint16_t* wr, double* out)
+{
+    for (int e = 0; e < E; ++e) {
+        double acc = 0.0;
+        for (int h = 0; h < H; ++h)
+            acc += orc_bf16_value(xrow[h]) * orc_bf16_value(wr[(int64_t)e * H + h]);
+        out[e] = acc;
+    }
+}
+
+/* Does expert a come before expert b in routing order?  Larger logit first;
+ * an exactly equal logit puts the lower index first. */
+static int route_before(const double* l, int a, int b)
+{
+#if ORC_PLANT == 2
+    if (l[a] == l[b]) return a > b; /* planted: ties go to the higher index */
+#else
+    if (l[a] == l[b]) return a < b;
+#endif
+    return l[a] > l[b];
+}
+
+/* Order all E experts by routing order (insertion sort), keep the first k as
+ * the slots, and weight them by a softmax over the k selected logits. */
+static void select_topk_one(int E, int k, const double* l, int32_t* idx, double* w, int* order)
+{
+    for (int e = 0; e < E; ++e) {
+        int pos = e;
+        while (pos > 0 && route_before(l, e, order[pos - 1])) {
+            order[pos] = order[pos - 1];
+            --pos;
+        }
+        order[pos] = e;
+    }
+    double lmax = l[order[0]];
+    double z = 0.0;
+    for (int j = 0; j < k; ++j) z += exp(l[order[j]] - lmax);
+    for (int j = 0; j < k; ++j) {
+        idx[j] = order[j];
+#if ORC_PLANT == 7
+        w[j] = exp(l[order[j]] - lmax); /* planted: weights not normalised */
+#else
+        w[j] = exp(l[order[j]] - lmax) / z;
+#endif
+    }
+}
+
+/* Route T tokens: logits [T][E] (optional), topk_idx [T][k], topk_w [T][k]. */
+int orc_route(int T, int H, int E, int k, const uint16_t* x, const uint16_t* wr,
+              double* logits, int32_t* topk_idx, double* topk_w, int threads)
+{
+    if (T < 0 || H <= 0 || E <= 0 || k < 1 || k > E || !x || !wr || !topk_idx || !topk_w)
+        return ORC_ERR_ARG;
+    int err = ORC_OK;
+#ifdef _OPENMP
+    if (threads > 0) omp_set_num_threads(threads);
+#else
+    (void)threads;
+#endif
+#pragma omp parallel
+    {
+        double* l = (double*)malloc(sizeof(double) * (size_t)E);
+        int* order = (int*)malloc(sizeof(int) * (size_t)E);
+        if (!l || !order) {
+#pragma omp atomic write
+            err = ORC_ERR_NOMEM;
+        }
+        /* every thread reaches the work-sharing loop; one without buffers skips its share */
+#pragma omp for schedule(static)
+        for (int t = 0; t < T; ++t) {
+            if (!l || !order) continue;
+            router_logits_one(H, E, x + (int64_t)t * H, wr, l);
+            if (logits) memcpy(logits + (int64_t)t * E, l, sizeof(double) * (size_t)E);
+            select_topk_one(E, k, l, topk_idx + (int64_t)t * k, topk_w + (int64_t)t * k, order);
+        }
+        free(l);
+        free(order);
+    }
+    return err;
+}
+
+/* ---------------------------------------------------------------- permute */
+
+/* Stable counting sort of the P = T*k pair ids by expert.
+ * expert_offsets [E+1]: exclusive prefix sum of the per-expert counts.
+ * sorted_pairs [P]: pair ids in expert-major order, ascending p inside each
+ * expert.  pair_rank [P]: the inverse, pair_rank[sorted_pairs[s]] = s. */
+int orc_permute(int T, int k, int E, const int32_t* topk_idx,
+                int32_t* expert_offsets, int32_t* sorted_pairs, int32_t* pair_rank)
+{
+    if (T < 0 || k < 1 || E <= 0 || !topk_idx || !expert_offsets || (T > 0 && (!sorted_pairs || !pair_rank)))
+        return ORC_ERR_ARG;
+    int64_t P = (int64_t)T * k;
+    int32_t* cursor = (int32_t*)calloc((size_t)E, sizeof(int32_t));
+    if (!cursor) return ORC_ERR_NOMEM;
+    for (int e = 0; e <= E; ++e) expert_offsets[e] = 0;
+    for (int64_t p = 0; p < P; ++p) {
+        int32_t e = topk_idx[p];
+        if (e < 0 || e >= E) {
+            free(cursor);
+            return ORC_ERR_ARG;
+        }
+        expert_offsets[e + 1] += 1;
+    }
+    for (int e = 0; e < E; ++e) expert_offsets[e + 1] += expert_offsets[e];
+    for (int e = 0; e < E; ++e) cursor[e] = expert_offsets[e];
+#if ORC_PLANT == 4
+    for (int64_t p = P - 1; p >= 0; --p) { /* planted: not stable */
+#else
+    for (int64_t p = 0; p < P; ++p) {
+#endif
+        int32_t e = topk_idx[p];
+        int32_t s = cursor[e]++;
+        sorted_pairs[s] = (int32_t)p;
+        pair_rank[p] = s;
+    }
+    free(cursor);
+    return ORC_OK;
+}
+
+/* ---------------------------------------------------------------- experts */
+
+static double silu(double z)
+{
+#if ORC_PLANT == 6
+    return z / (1.0 + exp(z)); /* planted: sign error */
+#else
+    return z / (1.0 + exp(-z));
+#endif
+}
+
+/* One expert on one token, with the expert's weights already decoded:
+ *   g_i = sum_h x_h Wgu[i][h],  u_i = sum_h x_h Wgu[I+i][h]   (i < I)
+ *   a_i = silu(g_i) * u_i
+ *   o_n = sum_i a_i Wd[n][i]                                  (n < H)
+ * h_out (I values) is optional. */
+static void expert_ffn_one(int H, int I, const double* xrow, const double* wgu, const double* wd,
+                           double* a, double* h_out, double* o_out)
+{
+    for (int i = 0; i < I; ++i) {
+        double g = 0.0, u = 0.0;
+#if ORC_PLANT == 1
+        const double* grow = wgu + (int64_t)(I + i) * H; /* planted: gate and up swapped */
+        const double* urow = wgu + (int64_t)i * H;
+#else
+        const double* grow = wgu + (int64_t)i * H;
+        const double* urow = wgu + (int64_t)(I + i) * H;
+#endif
+        for (int h = 0; h < H; ++h) g += xrow[h] * grow[h];
+        for (int h = 0; h < H; ++h) u += xrow[h] * urow[h];
+        a[i] = silu(g) * u;
+        if (h_out) h_out[i] = a[i];
+    }
+    for (int n = 0; n < H; ++n) {
+        double acc = 0.0;
+#if ORC_PLANT == 3
+        for (int i = 0; i < I; ++i) acc += a[i] * wd[(int64_t)i * H + n]; /* planted: Wd read transposed */
+#else
+        for (int i = 0; i < I; ++i) acc += a[i] * wd[(int64_t)n * I + i];
+#endif
+        o_out[n] = acc;
+    }
+}
+
+/* Expert outputs for a list of (token, expert) pairs.
+ * x bf16 [T][H]; gate_up [E][2I][H] (bf16) or [E][2I][H/2] + scales
+ * [E][2I][H/32] (MXFP4); down [E][H][I] or [E][H][I/2] + [E][H][I/32].
+ * h_out [npairs][I] (optional, SwiGLU output), o_out [npairs][H].
+ * Work is grouped by expert so each expert's weights are decoded once. */
+int orc_ffn_pairs(int H, int I, int E, int wfmt, const uint16_t* x,
+                  const void* gate_up, const uint8_t* gate_up_scale,
+                  const void* down, const uint8_t* down_scale,
+                  int npairs, const int32_t* pair_token, const int32_t* pair_expert,
+                  double* h_out, double* o_out, int threads)
+{
+    if (H <= 0 || I <= 0 || E <= 0 || npairs < 0 || !x || !gate_up || !down || !o_out ||
+        (npairs > 0 && (!pair_token || !pair_expert)))
+        return ORC_ERR_ARG;
+    if (wfmt != 0 && wfmt != 1) return ORC_ERR_ARG;
+    if (wfmt == 1 && (!gate_up_scale || !down_scale || H % 32 || I % 32)) return ORC_ERR_ARG;
+    for (int q = 0; q < npairs; ++q)
+        if (pair_expert[q] < 0 || pair_expert[q] >= E || pair_token[q] < 0) return ORC_ERR_ARG;
+#ifdef _OPENMP
+    if (threads > 0) omp_set_num_threads(threads);
+#else
+    (void)threads;
+#endif
+    double* wgu = (double*)malloc(sizeof(double) * (size_t)2 * I * H);
+    double* wd = (double*)malloc(sizeof(double) * (size_t)H * I);
+    int32_t* list = (int32_t*)malloc(sizeof(int32_t) * (size_t)(npairs > 0 ? npairs : 1));
+    if (!wgu || !wd || !list) {
+        free(wgu);
+        free(wd);
+        free(list);
+        return ORC_ERR_NOMEM;
+    }
+    int err = ORC_OK;
+    for (int e = 0; e < E && err == ORC_OK; ++e) {
+        int n = 0;
+        for (int q = 0; q < npairs; ++q)
+            if (pair_expert[q] == e) list[n++] = q;
+        if (n == 0) continue;
+        decode_expert_matrix(wfmt, gate_up, gate_up_scale, 2 * (int64_t)I, H, e, wgu);
+        decode_expert_matrix(wfmt, down, down_scale, H, I, e, wd);
+#pragma omp parallel
+        {
+            double* xr = (double*)malloc(sizeof(double) * (size_t)H);
+            double* a = (double*)malloc(sizeof(double) * (size_t)I);
+            if (!xr || !a) {
+#pragma omp atomic write
+                err = ORC_ERR_NOMEM;
+            }
+#pragma omp for schedule(dynamic, 1)
+            for (int j = 0; j < n; ++j) {
+                if (!xr || !a) continue;
+                int q = list[j];
+                const uint16_t* xs = x + (int64_t)pair_token[q] * H;
+                for (int h = 0; h < H; ++h) xr[h] = orc_bf16_value(xs[h]);
+                expert_ffn_one(H, I, xr, wgu, wd, a, h_out ? h_out + (int64_t)q * I : NULL,
+                               o_out + (int64_t)q * H);
+            }
+            free(xr);
+            free(a);
+        }
+    }
+    free(wgu);
+    free(wd);
+    free(list);
+    return err;
+}
+
+/* ---------------------------------------------------------------- layer */
+
+/* Whole layer for a subset of tokens (each token's output depends on that
+ * token alone):  y[t] = sum_j w[t][j] * expert_{idx[t][j]}(x[t]), the k terms
+ * added in slot order.  tokens [ntok] are row indices into x; y_out
+ * [ntok][H]; idx_out [ntok][k] and w_out [ntok][k] optional. */
+int orc_forward_tokens(int T, int H, int E, int k, int I, int wfmt,
+                       const uint16_t* x, const uint16_t* w_router,
+                       const void* gate_up, const uint8_t* gate_up_scale,
+                       const void* down, const uint8_t* down_scale,
+                       int ntok, const int32_t* tokens,
+                       double* y_out, int32_t* idx_out, double* w_out, int threads)
+{
+    if (T < 0 || H <= 0 || E <= 0 || k < 1 || k > E || I <= 0 || ntok < 0 || !x || !w_router || !y_out ||
+        (ntok > 0 && !tokens))
+        return ORC_ERR_ARG;
+    for (int i = 0; i < ntok; ++i)
+        if (tokens[i] < 0 || tokens[i] >= T) return ORC_ERR_ARG;
+    size_t nk = (size_t)(ntok > 0 ? ntok : 1) * (size_t)k;
+    uint16_t* xs = (uint16_t*)calloc((size_t)(ntok > 0 ? ntok : 1) * (size_t)H, sizeof(uint16_t));
+    int32_t* idx = (int32_t*)malloc(sizeof(int32_t) * nk);
+    double* w = (double*)malloc(sizeof(double) * nk);
+    int32_t* ptok = (int32_t*)malloc(sizeof(int32_t) * nk);
+    double* o = (double*)malloc(sizeof(double) * nk * (size_t)H);
+    int err = ORC_ERR_NOMEM;
+    if (xs && idx && w && ptok && o) {
+        for (int i = 0; i < ntok; ++i) memcpy(xs + (int64_t)i * H, x + (int64_t)tokens[i] * H, sizeof(uint16_t) * H);
+        err = orc_route(ntok, H, E, k, xs, w_router, NULL, idx, w, threads);
+        if (err == ORC_OK) {
+            for (int i = 0; i < ntok; ++i)
+                for (int j = 0; j < k; ++j) ptok[i * k + j] = i;
+            err = orc_ffn_pairs(H, I, E, wfmt, xs, gate_up, gate_up_scale, down, down_scale, ntok * k, ptok, idx,
+                                NULL, o, threads);
+        }
+        if (err == ORC_OK) {
+            for (int i = 0; i < ntok; ++i)
+                for (int n = 0; n < H; ++n) {
+                    double acc = 0.0;
+                    for (int j = 0; j < k; ++j) acc += w[i * k + j] * o[((int64_t)i * k + j) * H + n];
+                    y_out[(int64_t)i * H + n] = acc;
+                }
+            if (idx_out) memcpy(idx_out, idx, sizeof(int32_t) * (size_t)ntok * k);
+            if (w_out) memcpy(w_out, w, sizeof(double) * (size_t)ntok * k);
+        }
+    }
+    free(xs);
+    free(idx);
+    free(w);
+    free(ptok);
+    free(o);
+    return err;
+}
+
+/* Threads the OpenMP runtime will use for a parallel region (1 without it). */
+int orc_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

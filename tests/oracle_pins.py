@@ -1,0 +1,360 @@
+"""Pins for the CPU oracle: checks against things other than the oracle itself.
+
+Each pin takes an ``oracle.Oracle`` and raises AssertionError on failure, so the
+same pins run against the real oracle (tests/test_oracle_pins.py) and against
+builds with one planted mistake each (tests/test_oracle_mutants.py), which must
+each fail at least one pin.
+
+What pins what:
+  - decode: printed tables (tests/golden) for bf16 and E2M1, exhaustive
+    16 codes x 255 scales, the nibble-order reading, quantize->decode identity;
+  - route: brute force (an independent k-pass argmax over numpy logits),
+    constructed exact ties, all-zero router, sum of weights, k=1, the k=2
+    closed form, shift invariance, k=E full softmax;
+  - permute: inverse identity, histogram prefix, equality with a stable sort;
+  - experts + combine: E=1,k=1 reduces to the textbook dense SwiGLU FFN (numpy
+    matmuls, non-square H != I so a transposed operand shows), in bf16 and in
+    MXFP4 (decoded independently from the golden E2M1 table), identical
+    experts, k=E mixture, per-token independence, linearity in W_down,
+    silu(0)=0, and a whole layer worked by hand.
+"""
+from __future__ import annotations
+
+import math
+import os
+
+import numpy as np
+
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# --------------------------------------------------------------------------- fixtures
+
+
+def _golden_rows(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                rows.append(line.split())
+    return rows
+
+
+def golden_e2m1():
+    return {int(c): float(v) for c, v in _golden_rows("e2m1_codes.txt")}
+
+
+def golden_hand_layer():
+    return {r[0]: [float(v) for v in r[1:]] for r in _golden_rows("hand_layer_h2_i2_e3_k2.txt")}
+
+
+def _bf16(a):
+    return synth.bf16_from_f32(np.asarray(a, np.float32))
+
+
+def _rand_layer(seed, T, H, E, k, I, wfmt=0, w_std=0.05):
+    rng = np.random.default_rng(seed)
+    x = _bf16(rng.standard_normal((T, H)))
+    wr = _bf16(rng.standard_normal((E, H)) * w_std)
+    gu = rng.standard_normal((E, 2 * I, H)) * w_std
+    dn = rng.standard_normal((E, H, I)) * w_std
+    if wfmt == 0:
+        w = synth.Weights(0, _bf16(gu), _bf16(dn))
+    else:
+        q = [synth.mxfp4_quantize(gu[e]) for e in range(E)]
+        r = [synth.mxfp4_quantize(dn[e]) for e in range(E)]
+        w = synth.Weights(1, np.stack([a for a, _ in q]), np.stack([a for a, _ in r]),
+                          np.stack([b for _, b in q]), np.stack([b for _, b in r]))
+    return x, wr, w
+
+
+def _f64(b):
+    return synth.f32_from_bf16(b).astype(np.float64)
+
+
+def decode_independent(w: synth.Weights, which: str, e: int) -> np.ndarray:
+    """Decode one expert matrix without the oracle: bf16 by widening, MXFP4 by
+    the golden E2M1 table times 2^(S-127)."""
+    if w.wfmt == 0:
+        return _f64(getattr(w, which)[e])
+    data = getattr(w, which)[e]
+    scales = getattr(w, which + "_scale")[e]
+    table = golden_e2m1()
+    lut = np.array([table[c] for c in range(16)])
+    codes = np.empty((data.shape[0], data.shape[1] * 2), np.int64)
+    codes[:, 0::2] = data & 15
+    codes[:, 1::2] = data >> 4
+    sc = np.ldexp(1.0, scales.astype(np.int64) - 127)
+    return lut[codes] * np.repeat(sc, 32, axis=1)
+
+
+def dense_swiglu(xf, wgu, wd):
+    """Textbook dense SwiGLU FFN, numpy: (silu(X Wg^T) * (X Wu^T)) Wd^T."""
+    I = wd.shape[1]
+    g = xf @ wgu[:I].T
+    u = xf @ wgu[I:].T
+    return ((g / (1.0 + np.exp(-g))) * u) @ wd.T
+
+
+def _close(a, b, rtol=1e-12, atol=1e-12):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    scale = max(1.0, float(np.max(np.abs(b)))) if b.size else 1.0
+    err = float(np.max(np.abs(a - b))) if b.size else 0.0
+    assert err <= atol + rtol * scale, f"max |diff| {err:.3e} > {atol + rtol * scale:.3e}"
+
+
+# --------------------------------------------------------------------------- decode pins
+
+
+def pin_bf16_golden(o):
+    for hexbits, val in _golden_rows("bf16_values.txt"):
+        got = o.bf16_value(int(hexbits, 16))
+        assert got == float(val) and math.copysign(1, got) == math.copysign(1, float(val)), (hexbits, got, val)
+
+
+def pin_e2m1_golden(o):
+    for c, v in golden_e2m1().items():
+        got = o.e2m1_value(c)
+        assert got == v and math.copysign(1, got) == math.copysign(1, v), (c, got, v)
+
+
+def pin_mxfp4_exhaustive(o):
+    """All 16 codes x 255 finite scales, through the matrix decoder, against
+    golden E2M1 x 2^(S-127); S = 255 decodes to NaN."""
+    table = golden_e2m1()
+    codes = np.arange(16, dtype=np.uint8)
+    for s in range(256):
+        row = np.zeros((1, 16), np.uint8)  # 32 elements: code c at element 2c (low nibble)
+        row[0, :] = codes
+        sc = np.array([[s]], np.uint8)
+        got = o.decode_matrix(1, row[None], sc[None], 1, 32, 0)[0]
+        for c in range(16):
+            if s == 255:
+                assert math.isnan(got[2 * c]), (c, s)
+            else:
+                assert got[2 * c] == table[c] * math.ldexp(1.0, s - 127), (c, s, got[2 * c])
+            if s != 255:
+                assert got[2 * c + 1] == 0.0  # high nibbles hold code 0
+
+
+def pin_mxfp4_nibble_order(o):
+    """Element 2b is the low nibble of byte b, 2b+1 the high nibble; one scale
+    per 32 elements along the row."""
+    row = np.zeros((1, 1, 32), np.uint8)
+    row[0, 0, 0] = 0x72   # element 0 -> code 2 (1.0), element 1 -> code 7 (6.0)
+    row[0, 0, 16] = 0x9A  # element 32 -> code 10 (-1.0), element 33 -> code 9 (-0.5)
+    sc = np.array([[[127, 130]]], np.uint8)  # block 0: 2^0, block 1: 2^3
+    got = o.decode_matrix(1, row, sc, 1, 64, 0)[0]
+    assert got[0] == 1.0 and got[1] == 6.0, got[:2]
+    assert got[32] == -8.0 and got[33] == -4.0, got[32:34]
+
+
+def pin_quantize_decode_identity(o):
+    """Rows whose values lie on the MXFP4 grid (E2M1 value x 2^X, amax fixing
+    X) survive the generator's quantizer and the oracle's decoder unchanged."""
+    rng = np.random.default_rng(7)
+    table = golden_e2m1()
+    mags = np.array([table[c] for c in range(8)])
+    rows = []
+    for X in (-9, -5, 0, 3):
+        v = rng.choice(mags, size=(4, 64)) * rng.choice([-1.0, 1.0], size=(4, 64))
+        v[:, 0] = 6.0  # pins amax of block 0 so its shared exponent is X
+        v[:, 32] = -4.0  # block 1: amax 4 -> exponent floor(log2 4)-2 = 0
+        rows.append(v * math.ldexp(1.0, X))
+    w = np.concatenate(rows)
+    q, s = synth.mxfp4_quantize(w)
+    back = o.decode_matrix(1, q[None], s[None], w.shape[0], w.shape[1], 0)
+    assert np.array_equal(back, w)
+
+
+# --------------------------------------------------------------------------- route pins
+
+
+def _kpass_argmax(l, k):
+    """Independent top-k: k passes of argmax (numpy argmax returns the first,
+    i.e. lowest-index, maximum), removing the winner each time."""
+    l = l.copy()
+    out = []
+    for _ in range(k):
+        j = int(np.argmax(l))
+        out.append(j)
+        l[j] = -np.inf
+    return out
+
+
+def pin_route_bruteforce(o):
+    for seed, (T, H, E, k) in enumerate([(40, 24, 8, 3), (16, 64, 32, 4), (5, 32, 128, 4), (7, 16, 6, 6)]):
+        x, wr, _ = _rand_layer(seed, T, H, E, k, 32)
+        logits, idx, w = o.route(x, wr, k)
+        ref = _f64(x) @ _f64(wr).T
+        _close(logits, ref, rtol=1e-13)
+        for t in range(T):
+            assert list(idx[t]) == _kpass_argmax(ref[t], k), (t, idx[t])
+            sel = ref[t, idx[t]]
+            ew = np.exp(sel - sel.max())
+            _close(w[t], ew / ew.sum(), rtol=1e-13)
+
+
+def pin_route_exact_ties(o):
+    """Duplicate router rows give exactly equal logits; the lower index wins
+    and comes first.  Rows 2 and 5 become copies of the token's best row."""
+    x, wr, _ = _rand_layer(11, 8, 32, 8, 3, 32)
+    l = _f64(x) @ _f64(wr).T
+    for t in range(x.shape[0]):
+        best = int(np.argmax(l[t]))
+        wr2 = wr.copy()
+        wr2[2] = wr[best]
+        wr2[5] = wr[best]
+        _, idx, w = o.route(x[t:t + 1], wr2, 3)
+        if best in (2, 5):
+            assert list(idx[0][:2]) == [2, 5] and w[0][0] == w[0][1], (t, idx)
+        else:
+            assert list(idx[0]) == sorted([2, 5, best]), (t, best, idx)
+            assert w[0][0] == w[0][1] == w[0][2], w
+
+
+def pin_route_zero_router(o):
+    x, _, _ = _rand_layer(3, 4, 16, 8, 3, 32)
+    wr = np.zeros((8, 16), np.uint16)
+    _, idx, w = o.route(x, wr, 3)
+    assert (idx == np.array([0, 1, 2])).all()
+    assert (w == 1.0 / 3.0).all()
+
+
+def pin_route_weights(o):
+    x, wr, _ = _rand_layer(5, 64, 48, 16, 4, 32, w_std=0.2)
+    lg, idx, w = o.route(x, wr, 4)
+    assert np.all(np.abs(w.sum(1) - 1.0) <= 1e-12)
+    assert np.all(w > 0) and np.all(np.diff(w, axis=1) <= 0)  # descending-logit slots
+    _, idx1, w1 = o.route(x, wr, 1)
+    assert (w1 == 1.0).all() and (idx1[:, 0] == idx[:, 0]).all()
+    _, idx2, w2 = o.route(x, wr, 2)
+    l0 = lg[np.arange(64), idx2[:, 0]]
+    l1 = lg[np.arange(64), idx2[:, 1]]
+    _close(w2[:, 0], 1.0 / (1.0 + np.exp(l1 - l0)), rtol=1e-14)
+
+
+def pin_route_shift_invariance(o):
+    """A constant input channel with the same router weight c for every expert
+    adds c to every logit: the selection and the weights do not change."""
+    x, wr, _ = _rand_layer(9, 32, 31, 8, 3, 32)
+    _, idx, w = o.route(x, wr, 3)
+    xs = np.concatenate([x, np.full((32, 1), 0x3F80, np.uint16)], axis=1)  # channel of 1.0
+    wrs = np.concatenate([wr, np.full((8, 1), 0x4040, np.uint16)], axis=1)  # c = 3.0
+    _, idx2, w2 = o.route(xs, wrs, 3)
+    assert (idx == idx2).all()
+    _close(w2, w, rtol=1e-12)
+
+
+def pin_route_k_equals_E(o):
+    x, wr, _ = _rand_layer(13, 10, 40, 6, 6, 32, w_std=0.3)
+    lg, idx, w = o.route(x, wr, 6)
+    for t in range(10):
+        assert sorted(idx[t]) == list(range(6))
+        full = np.exp(lg[t] - lg[t].max())
+        full /= full.sum()
+        _close(w[t], full[idx[t]], rtol=1e-13)
+
+
+# --------------------------------------------------------------------------- permute pins
+
+
+def pin_permute(o):
+    rng = np.random.default_rng(21)
+    for T, k, E in [(37, 4, 32), (1, 4, 128), (64, 2, 8), (0, 4, 8), (100, 1, 3)]:
+        idx = np.array([rng.choice(E, size=k, replace=False) for _ in range(T)], np.int32).reshape(T, k)
+        off, sp, pr = o.permute(idx, E)
+        flat = idx.ravel()
+        assert (off == np.concatenate([[0], np.cumsum(np.bincount(flat, minlength=E))])).all()
+        assert (sp == np.argsort(flat, kind="stable")).all()
+        if T:
+            assert (pr[sp] == np.arange(T * k)).all() and (sp[pr] == np.arange(T * k)).all()
+            for e in range(E):
+                seg = sp[off[e]:off[e + 1]]
+                assert (np.diff(seg) > 0).all() and (flat[seg] == e).all()
+
+
+# --------------------------------------------------------------------------- expert pins
+
+
+def pin_dense_reduction(o):
+    """E=1, k=1: the layer is the textbook dense SwiGLU FFN (weight 1)."""
+    for wfmt in (0, 1):
+        T, H, I = 9, 64, 96
+        x, wr, w = _rand_layer(31 + wfmt, T, H, 1, 1, I, wfmt=wfmt)
+        y, idx, wts = o.forward_tokens(x, wr, w, 1, I, np.arange(T))
+        assert (idx == 0).all() and (wts == 1.0).all()
+        ref = dense_swiglu(_f64(x), decode_independent(w, "gate_up", 0), decode_independent(w, "down", 0))
+        _close(y, ref, rtol=1e-12)
+
+
+def pin_identical_experts(o):
+    """All experts equal: y is the dense FFN for any routing (weights sum to 1)."""
+    T, H, E, k, I = 12, 32, 6, 3, 64
+    x, wr, w = _rand_layer(41, T, H, E, k, I)
+    w = synth.Weights(0, np.repeat(w.gate_up[:1], E, 0).copy(), np.repeat(w.down[:1], E, 0).copy())
+    y, _, _ = o.forward_tokens(x, wr, w, k, I, np.arange(T))
+    ref = dense_swiglu(_f64(x), _f64(w.gate_up[0]), _f64(w.down[0]))
+    _close(y, ref, rtol=1e-12)
+
+
+def pin_mixture_k_equals_E(o):
+    """k = E: y = sum over all experts of full-softmax weight x expert FFN."""
+    T, H, E, I = 6, 32, 4, 48
+    x, wr, w = _rand_layer(43, T, H, E, E, I, w_std=0.1)
+    y, _, _ = o.forward_tokens(x, wr, w, E, I, np.arange(T))
+    xf = _f64(x)
+    lg = xf @ _f64(wr).T
+    p = np.exp(lg - lg.max(1, keepdims=True))
+    p /= p.sum(1, keepdims=True)
+    ref = sum(p[:, e:e + 1] * dense_swiglu(xf, _f64(w.gate_up[e]), _f64(w.down[e])) for e in range(E))
+    _close(y, ref, rtol=1e-12)
+
+
+def pin_token_independence_and_pairs(o):
+    """A token's output is the same alone or in a batch, and equals the
+    weighted sum of its per-pair expert outputs."""
+    T, H, E, k, I = 20, 32, 8, 2, 64
+    x, wr, w = _rand_layer(47, T, H, E, k, I)
+    y_all, idx, wts = o.forward_tokens(x, wr, w, k, I, np.arange(T))
+    sub = np.array([3, 17, 4])
+    y_sub, _, _ = o.forward_tokens(x, wr, w, k, I, sub)
+    assert np.array_equal(y_sub, y_all[sub])
+    y_one, _, _ = o.forward_tokens(x[5:6], wr, w, k, I, np.array([0]))
+    assert np.array_equal(y_one[0], y_all[5])
+    pt = np.repeat(np.arange(T), k)
+    oo = o.ffn_pairs(x, w, I, E, pt, idx.ravel())
+    ref = (wts.reshape(T, k, 1) * oo.reshape(T, k, H)).sum(1)
+    _close(y_all, ref, rtol=1e-13)
+
+
+def pin_linearity_and_silu_zero(o):
+    T, H, E, k, I = 8, 32, 4, 2, 32
+    x, wr, w = _rand_layer(53, T, H, E, k, I)
+    y, _, _ = o.forward_tokens(x, wr, w, k, I, np.arange(T))
+    w2 = synth.Weights(0, w.gate_up, _bf16(_f64(w.down) * 2.0))
+    y2, _, _ = o.forward_tokens(x, wr, w2, k, I, np.arange(T))
+    assert np.array_equal(y2, 2.0 * y)
+    gz = w.gate_up.copy()
+    gz[:, :I, :] = 0  # gate rows zero -> silu(0) = 0 -> y = 0
+    y0, _, _ = o.forward_tokens(x, wr, synth.Weights(0, gz, w.down), k, I, np.arange(T))
+    assert not np.any(y0)
+
+
+def pin_hand_layer(o):
+    g = golden_hand_layer()
+    x = _bf16([g["x"]])
+    wr = _bf16(np.array(g["router"]).reshape(3, 2))
+    gu = _bf16(np.stack([np.array(g[f"gate_up_e{e}"]).reshape(4, 2) for e in range(3)]))
+    dn = _bf16(np.stack([np.array(g[f"down_e{e}"]).reshape(2, 2) for e in range(3)]))
+    y, idx, w = o.forward_tokens(x, wr, synth.Weights(0, gu, dn), 2, 2, np.array([0]))
+    assert list(idx[0]) == [int(v) for v in g["topk_idx"]]
+    _close(w[0], g["topk_w"], rtol=1e-15, atol=0)
+    _close(y[0], g["y"], rtol=1e-14, atol=0)
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
