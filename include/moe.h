@@ -1,0 +1,174 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) Mixture-of-Experts FFN layer library.
+ *
+ * The layer is the gpt-oss expert block: each token is routed to the top k of
+ * E experts by a linear router, each selected expert applies a SwiGLU FFN, and
+ * the k expert outputs are summed with the routing weights.  The pages fix the
+ * shapes and number formats:
+ *   - hidden 2880, top-4 of 32 experts, SwiGLU experts: "Persona Kappa:
+ *     training a 20B LLM on desktop GPUs" (Level1Techs forum), table
+ *     "Architecture Summary";
+ *   - 4 of 128 experts for the 120b model, ~1 token per expert at 12-16
+ *     streams: "hearth-lean-loomed-v1" model card, section "Why 12-16 streams
+ *     can be slow on Vulkan";
+ *   - expert weights natively MXFP4, activations kept in bf16 (W4A16), and
+ *     2880 not a multiple of 128: Persona Kappa post, section
+ *     "Quantization-Aware Training (QAT)"; "gpt-oss-20b" model page, section
+ *     "Architecture";
+ *   - bf16 forward with fp32 accumulation: Persona Kappa post, section
+ *     "Techniques That Made It Fit".
+ * The pages give no formulas; the library computes (T tokens, H hidden, E
+ * experts, k per token, I expert width, P = T*k pairs):
+ *   l[t][e]   = sum_h x[t][h] * W_router[e][h]
+ *   slots     = the k experts with the largest l[t][.], largest first; an
+ *               exactly equal logit goes to the lower expert index
+ *   w[t][j]   = exp(l_j - l_0) / sum_i exp(l_i - l_0) over the k slots
+ *   pair p    = t*k + j, routed to expert topk_idx[t][j]
+ *   g, u      = x[t] . W_gate_up[e][0..I-1][:],  x[t] . W_gate_up[e][I..2I-1][:]
+ *   h         = silu(g) * u,   silu(z) = z / (1 + exp(-z))
+ *   o         = W_down[e] . h
+ *   y[t]      = sum_j w[t][j] * o_{t,j}        (j in slot order)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers are DEVICE pointers (HIP global memory) unless stated otherwise;
+ * `dims` and `weights` structs are HOST memory read during the call.
+ * All matrices are row-major with the last index contiguous.  bf16 buffers
+ * hold raw bfloat16 bit patterns.
+ *
+ *   x              bf16  [T][H]
+ *   w_router       bf16  [E][H]
+ *   gate_up  bf16  bf16  [E][2I][H]     rows 0..I-1 gate, rows I..2I-1 up
+ *   down     bf16  bf16  [E][H][I]
+ *   gate_up  MXFP4 u8    [E][2I][H/2]   + gate_up_scale u8 [E][2I][H/32]
+ *   down     MXFP4 u8    [E][H][I/2]    + down_scale    u8 [E][H][I/32]
+ *            (OCP MX: E2M1 element 2b in the low nibble of byte b, element
+ *             2b+1 in the high nibble; one E8M0 scale 2^(S-127) per 32
+ *             consecutive elements along the input dimension)
+ *   topk_idx       int32 [T][k]   slots in routing order
+ *   topk_w         fp32  [T][k]
+ *   expert_offsets int32 [E+1]    exclusive prefix sum of pairs per expert
+ *   sorted_pairs   int32 [P]      pair ids p, expert-major, ascending p within
+ *                                 an expert (a stable sort by expert)
+ *   pair_rank      int32 [P]      inverse: pair_rank[sorted_pairs[s]] = s
+ *   h              bf16  [P][I]   SwiGLU output, row s = sorted position
+ *   y_sorted       bf16  [P][H]   unweighted expert outputs, row s = sorted position
+ *   y              bf16  [T][H]
+ *
+ * Alignment: bf16 matrices, weight bytes and the workspace must be 16-byte
+ * aligned; int32/fp32 arrays 4-byte aligned; scale arrays need no alignment.
+ * Supported sizes: 1 <= E <= 256, 1 <= k <= min(E, 8), H and I multiples of
+ * 32, T >= 0 with T*k < 2^31.  T = 0 returns MOE_OK and launches nothing.
+ *
+ * Ownership: the caller owns every buffer, including the workspace (size from
+ * moe_workspace_size).  The library allocates nothing, frees nothing and keeps
+ * no state between calls.  Outputs must not alias inputs.
+ *
+ * Asynchrony: each call validates its arguments on the host, then only
+ * enqueues kernels on `stream` (a hipStream_t passed as void*; NULL = the
+ * default stream) and returns; there is no host synchronisation and no
+ * device-to-host copy.  Buffers must stay valid until the stream has run the
+ * work.  Results are deterministic: the same inputs give bitwise-identical
+ * outputs (no split-K, no floating-point atomics).
+ *
+ * Errors: every call returns an int (MOE_OK or an error code below).  All
+ * validation happens before the first launch: on error nothing is launched
+ * and no output is touched.  A launch failure returns MOE_ERR_HIP; the HIP
+ * error text is kept per thread for moe_last_error().  No C++ exception
+ * crosses this interface.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1, /* null pointer, negative size, k < 1 or k > E, T*k overflow */
+    MOE_ERR_UNSUPPORTED = 2, /* E > 256, k > 8, H or I not a multiple of 32, unknown wfmt/path */
+    MOE_ERR_MISALIGNED = 3,  /* a pointer breaks the alignment rules above */
+    MOE_ERR_WORKSPACE = 4,   /* workspace smaller than moe_workspace_size() */
+    MOE_ERR_HIP = 5          /* a HIP launch failed; see moe_last_error() */
+};
+
+enum { MOE_WFMT_BF16 = 0, MOE_WFMT_MXFP4 = 1 };
+
+/* Expert-FFN schedule.  AUTO picks SKINNY when tokens per expert are few
+ * (weight streaming at HBM rate) and TILED otherwise (LDS-tiled grouped GEMM).
+ * Both compute the same function; forcing one is for testing and tuning. */
+enum { MOE_PATH_AUTO = 0, MOE_PATH_SKINNY = 1, MOE_PATH_TILED = 2 };
+
+typedef struct moe_dims {
+    int32_t T, H, E, k, I;
+    int32_t wfmt; /* MOE_WFMT_* : format of gate_up and down */
+    int32_t path; /* MOE_PATH_* */
+} moe_dims;
+
+typedef struct moe_expert_weights {
+    const void* gate_up;          /* see layouts above */
+    const uint8_t* gate_up_scale; /* MXFP4 only, else NULL */
+    const void* down;
+    const uint8_t* down_scale;    /* MXFP4 only, else NULL */
+} moe_expert_weights;
+
+/* Workspace bytes needed by every entry point below for these dims (the
+ * largest, moe_forward's, covers all).  Host-only; launches nothing. */
+int moe_workspace_size(const moe_dims* dims, size_t* bytes);
+
+/* Router (logits, top-k selection, softmax over the k selected).
+ * Reads x, w_router; writes topk_idx [T][k], topk_w [T][k].
+ * Selection is made on logits equal to the exactly-rounded sum (decided in
+ * fp64), so indices match a double-precision reference bit for bit. */
+int moe_route(const moe_dims* dims, const void* x, const void* w_router, int32_t* topk_idx, float* topk_w,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Permutation of the P pairs into expert-contiguous segments (stable counting
+ * sort by expert).  Reads topk_idx; writes expert_offsets [E+1],
+ * sorted_pairs [P], pair_rank [P].  topk_idx values outside [0, E) are
+ * undefined behaviour (the router never produces them). */
+int moe_permute(const moe_dims* dims, const int32_t* topk_idx, int32_t* expert_offsets, int32_t* sorted_pairs,
+                int32_t* pair_rank, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Gate/up projection with the fused SwiGLU epilogue, per expert segment:
+ * h[s] = silu(x[t] . Wg^T) * (x[t] . Wu^T) for sorted position s of pair
+ * p = sorted_pairs[s], t = p / k.  Writes h [P][I] (bf16, fp32 accumulate). */
+int moe_gate_up(const moe_dims* dims, const void* x, const int32_t* expert_offsets, const int32_t* sorted_pairs,
+                const moe_expert_weights* weights, void* h, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Down projection per expert segment: y_sorted[s] = W_down[e] . h[s] for
+ * every s in expert e's segment.  Writes y_sorted [P][H] (bf16, unweighted). */
+int moe_down(const moe_dims* dims, const void* h, const int32_t* expert_offsets, const moe_expert_weights* weights,
+             void* y_sorted, void* workspace, size_t workspace_bytes, void* stream);
+
+/* moe_gate_up followed by moe_down, with h kept in the workspace. */
+int moe_grouped_ffn(const moe_dims* dims, const void* x, const int32_t* expert_offsets, const int32_t* sorted_pairs,
+                    const moe_expert_weights* weights, void* y_sorted, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/* Weighted combine: y[t] = sum_j topk_w[t][j] * y_sorted[pair_rank[t*k+j]],
+ * summed in fp32 in slot order, rounded to bf16 (nearest-even). */
+int moe_combine(const moe_dims* dims, const void* y_sorted, const int32_t* pair_rank, const float* topk_w, void* y,
+                void* stream);
+
+/* The whole layer: route, permute, gate/up + SwiGLU, down, combine.
+ * topk_idx_out / topk_w_out may be NULL (then they live in the workspace);
+ * when given they receive the routing. */
+int moe_forward(const moe_dims* dims, const void* x, const void* w_router, const moe_expert_weights* weights, void* y,
+                int32_t* topk_idx_out, float* topk_w_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static text for an error code. */
+const char* moe_strerror(int code);
+
+/* Text of the last MOE_ERR_HIP raised on the calling thread ("" if none). */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

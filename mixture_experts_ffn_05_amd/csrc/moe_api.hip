@@ -1,0 +1,312 @@
+// C ABI of the MoE FFN library: argument validation, workspace layout,
+// schedule choice and kernel launches.  Declarations and contracts are in
+// include/moe.h.  Nothing here allocates, synchronises or copies to the host.
+#include <string.h>
+
+#include <string>
+
+#include "moe.h"
+#include "moe_kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Workspace regions (byte offsets from the workspace base).  Every entry
+// point uses this one layout, so one workspace of moe_workspace_size() bytes
+// serves all of them.
+struct Layout {
+    size_t topk_idx, topk_w, logits, offsets, sorted, rank, perm_scratch, h, y_sorted, total;
+};
+
+Layout layout_for(const moe_dims& d)
+{
+    const size_t T = (size_t)d.T, P = (size_t)d.T * (size_t)d.k;
+    Layout L;
+    size_t at = 0;
+    auto take = [&](size_t bytes) {
+        size_t here = at;
+        at = align_up(at + bytes);
+        return here;
+    };
+    L.topk_idx = take(P * sizeof(int32_t));
+    L.topk_w = take(P * sizeof(float));
+    L.logits = take(T * (size_t)d.E * sizeof(double));
+    L.offsets = take(((size_t)d.E + 1) * sizeof(int32_t));
+    L.sorted = take(P * sizeof(int32_t));
+    L.rank = take(P * sizeof(int32_t));
+    L.perm_scratch = take(moe::permute_scratch_bytes((int64_t)P, d.E));
+    L.h = take(P * (size_t)d.I * 2);
+    L.y_sorted = take(P * (size_t)d.H * 2);
+    L.total = at;
+    return L;
+}
+
+int check_dims(const moe_dims* d)
+{
+    if (!d) return MOE_ERR_INVALID_ARG;
+    if (d->T < 0 || d->H <= 0 || d->E <= 0 || d->k < 1 || d->I <= 0 || d->k > d->E) return MOE_ERR_INVALID_ARG;
+    if ((int64_t)d->T * d->k > INT32_MAX) return MOE_ERR_INVALID_ARG;
+    if (d->E > 256 || d->k > 8) return MOE_ERR_UNSUPPORTED;
+    if (d->H % 32 != 0 || d->I % 32 != 0) return MOE_ERR_UNSUPPORTED;
+    if (d->wfmt != MOE_WFMT_BF16 && d->wfmt != MOE_WFMT_MXFP4) return MOE_ERR_UNSUPPORTED;
+    if (d->path != MOE_PATH_AUTO && d->path != MOE_PATH_SKINNY && d->path != MOE_PATH_TILED)
+        return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Null check + alignment check of a device pointer.
+int check_ptr(const void* p, size_t a)
+{
+    if (!p) return MOE_ERR_INVALID_ARG;
+    return aligned(p, a) ? MOE_OK : MOE_ERR_MISALIGNED;
+}
+
+int check_weights(const moe_dims& d, const moe_expert_weights* w)
+{
+    if (!w) return MOE_ERR_INVALID_ARG;
+    int rc;
+    if ((rc = check_ptr(w->gate_up, 16)) || (rc = check_ptr(w->down, 16))) return rc;
+    if (d.wfmt == MOE_WFMT_MXFP4 && (!w->gate_up_scale || !w->down_scale)) return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
+int check_ws(const moe_dims& d, const void* ws, size_t ws_bytes)
+{
+    if (ws_bytes < layout_for(d).total) return MOE_ERR_WORKSPACE;
+    return check_ptr(ws, 16);
+}
+
+int hip_status(hipError_t e)
+{
+    if (e == hipSuccess) return MOE_OK;
+    g_last_error = hipGetErrorString(e);
+    return MOE_ERR_HIP;
+}
+
+template <typename T>
+T* region(void* ws, size_t off)
+{
+    return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+// Skinny (weight streaming) while an expert can see at most this many tokens:
+// per-expert token counts never exceed T, and up to 64 tokens the skinny
+// kernels stay bound by weight traffic.
+constexpr int kSkinnyMaxT = 64;
+
+bool use_skinny(const moe_dims& d)
+{
+    if (d.path == MOE_PATH_SKINNY) return true;
+    if (d.path == MOE_PATH_TILED) return false;
+    return d.T <= kSkinnyMaxT;
+}
+
+moe::FfnArgs ffn_args(const moe_dims& d)
+{
+    moe::FfnArgs a;
+    memset(&a, 0, sizeof a);
+    a.T = d.T;
+    a.H = d.H;
+    a.E = d.E;
+    a.k = d.k;
+    a.I = d.I;
+    a.wfmt = d.wfmt;
+    return a;
+}
+
+// ---- stage bodies (arguments already validated) ----
+
+int do_route(const moe_dims& d, const void* x, const void* wr, int32_t* idx, float* w, void* ws, hipStream_t s)
+{
+    const Layout L = layout_for(d);
+    double* logits = region<double>(ws, L.logits);
+    int rc = hip_status(moe::launch_router_logits_f64(d.T, d.H, d.E, static_cast<const uint16_t*>(x),
+                                                      static_cast<const uint16_t*>(wr), logits, s));
+    if (rc) return rc;
+    return hip_status(moe::launch_router_select(d.T, d.E, d.k, logits, idx, w, s));
+}
+
+int do_permute(const moe_dims& d, const int32_t* idx, int32_t* off, int32_t* sp, int32_t* pr, void* ws, hipStream_t s)
+{
+    const Layout L = layout_for(d);
+    return hip_status(moe::launch_permute(d.T * d.k, d.E, idx, off, sp, pr, region<void>(ws, L.perm_scratch), s));
+}
+
+int do_gate_up(const moe_dims& d, const void* x, const int32_t* off, const int32_t* sp, const moe_expert_weights& w,
+               void* h, hipStream_t s)
+{
+    moe::FfnArgs a = ffn_args(d);
+    a.x = static_cast<const uint16_t*>(x);
+    a.offsets = off;
+    a.sorted_pairs = sp;
+    a.w = w.gate_up;
+    a.w_scale = w.gate_up_scale;
+    a.out = static_cast<uint16_t*>(h);
+    return hip_status(use_skinny(d) ? moe::launch_gate_up_skinny(a, s) : moe::launch_gate_up_tiled(a, s));
+}
+
+int do_down(const moe_dims& d, const void* h, const int32_t* off, const moe_expert_weights& w, void* ys, hipStream_t s)
+{
+    moe::FfnArgs a = ffn_args(d);
+    a.offsets = off;
+    a.a_rows = static_cast<const uint16_t*>(h);
+    a.w = w.down;
+    a.w_scale = w.down_scale;
+    a.out = static_cast<uint16_t*>(ys);
+    return hip_status(use_skinny(d) ? moe::launch_down_skinny(a, s) : moe::launch_down_tiled(a, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_workspace_size(const moe_dims* dims, size_t* bytes)
+{
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    if (!bytes) return MOE_ERR_INVALID_ARG;
+    *bytes = layout_for(*dims).total;
+    return MOE_OK;
+}
+
+int moe_route(const moe_dims* dims, const void* x, const void* w_router, int32_t* topk_idx, float* topk_w,
+              void* workspace, size_t workspace_bytes, void* stream)
+{
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    const moe_dims& d = *dims;
+    if (d.T == 0) return MOE_OK;
+    if ((rc = check_ptr(x, 16)) || (rc = check_ptr(w_router, 16)) || (rc = check_ptr(topk_idx, 4)) ||
+        (rc = check_ptr(topk_w, 4)) || (rc = check_ws(d, workspace, workspace_bytes)))
+        return rc;
+    return do_route(d, x, w_router, topk_idx, topk_w, workspace, static_cast<hipStream_t>(stream));
+}
+
+int moe_permute(const moe_dims* dims, const int32_t* topk_idx, int32_t* expert_offsets, int32_t* sorted_pairs,
+                int32_t* pair_rank, void* workspace, size_t workspace_bytes, void* stream)
+{
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    const moe_dims& d = *dims;
+    if (d.T == 0) return MOE_OK;
+    if ((rc = check_ptr(topk_idx, 4)) || (rc = check_ptr(expert_offsets, 4)) || (rc = check_ptr(sorted_pairs, 4)) ||
+        (rc = check_ptr(pair_rank, 4)) || (rc = check_ws(d, workspace, workspace_bytes)))
+        return rc;
+    return do_permute(d, topk_idx, expert_offsets, sorted_pairs, pair_rank, workspace,
+                      static_cast<hipStream_t>(stream));
+}
+
+int moe_gate_up(const moe_dims* dims, const void* x, const int32_t* expert_offsets, const int32_t* sorted_pairs,
+                const moe_expert_weights* weights, void* h, void* workspace, size_t workspace_bytes, void* stream)
+{
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    const moe_dims& d = *dims;
+    if (d.T == 0) return MOE_OK;
+    if ((rc = check_ptr(x, 16)) || (rc = check_ptr(expert_offsets, 4)) || (rc = check_ptr(sorted_pairs, 4)) ||
+        (rc = check_weights(d, weights)) || (rc = check_ptr(h, 16)))
+        return rc;
+    (void)workspace;
+    (void)workspace_bytes;
+    return do_gate_up(d, x, expert_offsets, sorted_pairs, *weights, h, static_cast<hipStream_t>(stream));
+}
+
+int moe_down(const moe_dims* dims, const void* h, const int32_t* expert_offsets, const moe_expert_weights* weights,
+             void* y_sorted, void* workspace, size_t workspace_bytes, void* stream)
+{
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    const moe_dims& d = *dims;
+    if (d.T == 0) return MOE_OK;
+    if ((rc = check_ptr(h, 16)) || (rc = check_ptr(expert_offsets, 4)) || (rc = check_weights(d, weights)) ||
+        (rc = check_ptr(y_sorted, 16)))
+        return rc;
+    (void)workspace;
+    (void)workspace_bytes;
+    return do_down(d, h, expert_offsets, *weights, y_sorted, static_cast<hipStream_t>(stream));
+}
+
+int moe_grouped_ffn(const moe_dims* dims, const void* x, const int32_t* expert_offsets, const int32_t* sorted_pairs,
+                    const moe_expert_weights* weights, void* y_sorted, void* workspace, size_t workspace_bytes,
+                    void* stream)
+{
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    const moe_dims& d = *dims;
+    if (d.T == 0) return MOE_OK;
+    if ((rc = check_ptr(x, 16)) || (rc = check_ptr(expert_offsets, 4)) || (rc = check_ptr(sorted_pairs, 4)) ||
+        (rc = check_weights(d, weights)) || (rc = check_ptr(y_sorted, 16)) ||
+        (rc = check_ws(d, workspace, workspace_bytes)))
+        return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void* h = region<void>(workspace, layout_for(d).h);
+    if ((rc = do_gate_up(d, x, expert_offsets, sorted_pairs, *weights, h, s))) return rc;
+    return do_down(d, h, expert_offsets, *weights, y_sorted, s);
+}
+
+int moe_combine(const moe_dims* dims, const void* y_sorted, const int32_t* pair_rank, const float* topk_w, void* y,
+                void* stream)
+{
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    const moe_dims& d = *dims;
+    if (d.T == 0) return MOE_OK;
+    if ((rc = check_ptr(y_sorted, 16)) || (rc = check_ptr(pair_rank, 4)) || (rc = check_ptr(topk_w, 4)) ||
+        (rc = check_ptr(y, 16)))
+        return rc;
+    return hip_status(moe::launch_combine(d.T, d.H, d.k, static_cast<const uint16_t*>(y_sorted), pair_rank, topk_w,
+                                          static_cast<uint16_t*>(y), static_cast<hipStream_t>(stream)));
+}
+
+int moe_forward(const moe_dims* dims, const void* x, const void* w_router, const moe_expert_weights* weights, void* y,
+                int32_t* topk_idx_out, float* topk_w_out, void* workspace, size_t workspace_bytes, void* stream)
+{
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    const moe_dims& d = *dims;
+    if (d.T == 0) return MOE_OK;
+    if ((rc = check_ptr(x, 16)) || (rc = check_ptr(w_router, 16)) || (rc = check_weights(d, weights)) ||
+        (rc = check_ptr(y, 16)) || (rc = check_ws(d, workspace, workspace_bytes)))
+        return rc;
+    if ((topk_idx_out && !aligned(topk_idx_out, 4)) || (topk_w_out && !aligned(topk_w_out, 4)))
+        return MOE_ERR_MISALIGNED;
+    const Layout L = layout_for(d);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int32_t* idx = topk_idx_out ? topk_idx_out : region<int32_t>(workspace, L.topk_idx);
+    float* w = topk_w_out ? topk_w_out : region<float>(workspace, L.topk_w);
+    int32_t* off = region<int32_t>(workspace, L.offsets);
+    int32_t* sp = region<int32_t>(workspace, L.sorted);
+    int32_t* pr = region<int32_t>(workspace, L.rank);
+    void* h = region<void>(workspace, L.h);
+    void* ys = region<void>(workspace, L.y_sorted);
+    if ((rc = do_route(d, x, w_router, idx, w, workspace, s))) return rc;
+    if ((rc = do_permute(d, idx, off, sp, pr, workspace, s))) return rc;
+    if ((rc = do_gate_up(d, x, off, sp, *weights, h, s))) return rc;
+    if ((rc = do_down(d, h, off, *weights, ys, s))) return rc;
+    return hip_status(moe::launch_combine(d.T, d.H, d.k, static_cast<const uint16_t*>(ys), pr, w,
+                                          static_cast<uint16_t*>(y), s));
+}
+
+const char* moe_strerror(int code)
+{
+    switch (code) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported size or format";
+    case MOE_ERR_MISALIGNED: return "misaligned pointer";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP launch failed";
+    default: return "unknown error";
+    }
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,48 @@
+// Host-side launchers of the gfx950 kernels (one .hip file per stage).
+// Each returns the hipError_t of its launches; arguments are validated by the
+// C-ABI layer (moe_api.hip) before any of these run.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ------------------------------------------------------------------ route
+// Exact logits (fp64 accumulation of exact bf16 products), one wave per
+// (token, group of experts).  logits [T][E] fp64.
+hipError_t launch_router_logits_f64(int T, int H, int E, const uint16_t* x, const uint16_t* wr, double* logits,
+                                    hipStream_t s);
+// Top-k by logit (ties -> lower index) + softmax over the k, one wave per token.
+hipError_t launch_router_select(int T, int E, int k, const double* logits, int32_t* topk_idx, float* topk_w,
+                                hipStream_t s);
+
+// ------------------------------------------------------------------ permute
+constexpr int PERMUTE_CHUNK = 1024;  // pairs ranked per workgroup pass
+// Workspace for the multi-block permutation: rank [P] + hist [ceil(P/1024)][E] int32.
+size_t permute_scratch_bytes(int64_t P, int E);
+hipError_t launch_permute(int P, int E, const int32_t* topk_idx, int32_t* offsets, int32_t* sorted_pairs,
+                          int32_t* pair_rank, void* scratch, hipStream_t s);
+
+// ------------------------------------------------------------------ expert FFN
+struct FfnArgs {
+    int T, H, E, k, I, wfmt;
+    const uint16_t* x;          // [T][H] (gate/up input, gathered)
+    const int32_t* offsets;     // [E+1]
+    const int32_t* sorted_pairs;  // [P]
+    const void* w;              // gate_up or down
+    const uint8_t* w_scale;     // MXFP4 scales or null
+    const uint16_t* a_rows;     // down: h [P][I] (sorted rows)
+    uint16_t* out;              // gate/up: h [P][I]; down: y_sorted [P][H]
+};
+hipError_t launch_gate_up_skinny(const FfnArgs& a, hipStream_t s);
+hipError_t launch_down_skinny(const FfnArgs& a, hipStream_t s);
+hipError_t launch_gate_up_tiled(const FfnArgs& a, hipStream_t s);
+hipError_t launch_down_tiled(const FfnArgs& a, hipStream_t s);
+
+// ------------------------------------------------------------------ combine
+hipError_t launch_combine(int T, int H, int k, const uint16_t* y_sorted, const int32_t* pair_rank,
+                          const float* topk_w, uint16_t* y, hipStream_t s);
+
+}  // namespace moe

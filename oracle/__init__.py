@@ -58,7 +58,8 @@ def _bind(lib):
     lib.orc_ffn_pairs.restype = _I
     lib.orc_ffn_pairs.argtypes = [_I, _I, _I, _I, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _I]
     lib.orc_forward_tokens.restype = _I
-    lib.orc_forward_tokens.argtypes = [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _I]
+    lib.orc_forward_tokens.argtypes = [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P,
+                                        _I]
     lib.orc_max_threads.restype = _I
     lib.orc_max_threads.argtypes = []
     return lib
@@ -139,8 +140,9 @@ class Oracle:
                                            self._ptr(h), self._ptr(o), threads), "ffn_pairs")
         return (o, h) if want_h else o
 
-    def forward_tokens(self, x, w_router, weights, k: int, I: int, tokens, threads: int = 0):
-        """Layer output for the listed tokens: returns (y [n][H], idx [n][k], w [n][k])."""
+    def forward_tokens(self, x, w_router, weights, k: int, I: int, tokens, threads: int = 0, want_pairs=False):
+        """Layer output for the listed tokens: returns (y [n][H], idx [n][k], w [n][k]), and with
+        want_pairs also the per-slot expert outputs o [n][k][H] and SwiGLU activations h [n][k][I]."""
         T, H = x.shape
         E = w_router.shape[0]
         tok = np.ascontiguousarray(tokens, np.int32)
@@ -148,12 +150,15 @@ class Oracle:
         y = np.empty((n, H), np.float64)
         idx = np.empty((n, k), np.int32)
         w = np.empty((n, k), np.float64)
+        o = np.empty((n, k, H), np.float64) if want_pairs else None
+        h = np.empty((n, k, I), np.float64) if want_pairs else None
         self._check(self.lib.orc_forward_tokens(T, H, E, k, I, weights.wfmt, self._ptr(x), self._ptr(w_router),
                                                 self._ptr(weights.gate_up), self._ptr(weights.gate_up_scale),
                                                 self._ptr(weights.down), self._ptr(weights.down_scale), n,
-                                                self._ptr(tok), self._ptr(y), self._ptr(idx), self._ptr(w), threads),
+                                                self._ptr(tok), self._ptr(y), self._ptr(idx), self._ptr(w),
+                                                self._ptr(o), self._ptr(h), threads),
                     "forward_tokens")
-        return y, idx, w
+        return (y, idx, w, o, h) if want_pairs else (y, idx, w)
 
     def max_threads(self) -> int:
         return self.lib.orc_max_threads()

@@ -355,13 +355,15 @@ int orc_ffn_pairs(int H, int I, int E, int wfmt, const uint16_t* x,
 /* Whole layer for a subset of tokens (each token's output depends on that
  * token alone):  y[t] = sum_j w[t][j] * expert_{idx[t][j]}(x[t]), the k terms
  * added in slot order.  tokens [ntok] are row indices into x; y_out
- * [ntok][H]; idx_out [ntok][k] and w_out [ntok][k] optional. */
+ * [ntok][H].  Optional: idx_out [ntok][k], w_out [ntok][k], the per-slot
+ * expert outputs o_out [ntok][k][H] and SwiGLU activations h_out [ntok][k][I]. */
 int orc_forward_tokens(int T, int H, int E, int k, int I, int wfmt,
                        const uint16_t* x, const uint16_t* w_router,
                        const void* gate_up, const uint8_t* gate_up_scale,
                        const void* down, const uint8_t* down_scale,
                        int ntok, const int32_t* tokens,
-                       double* y_out, int32_t* idx_out, double* w_out, int threads)
+                       double* y_out, int32_t* idx_out, double* w_out,
+                       double* o_out, double* h_out, int threads)
 {
     if (T < 0 || H <= 0 || E <= 0 || k < 1 || k > E || I <= 0 || ntok < 0 || !x || !w_router || !y_out ||
         (ntok > 0 && !tokens))
@@ -382,7 +384,7 @@ int orc_forward_tokens(int T, int H, int E, int k, int I, int wfmt,
             for (int i = 0; i < ntok; ++i)
                 for (int j = 0; j < k; ++j) ptok[i * k + j] = i;
             err = orc_ffn_pairs(H, I, E, wfmt, xs, gate_up, gate_up_scale, down, down_scale, ntok * k, ptok, idx,
-                                NULL, o, threads);
+                                h_out, o, threads);
         }
         if (err == ORC_OK) {
             for (int i = 0; i < ntok; ++i)
@@ -393,6 +395,7 @@ int orc_forward_tokens(int T, int H, int E, int k, int I, int wfmt,
                 }
             if (idx_out) memcpy(idx_out, idx, sizeof(int32_t) * (size_t)ntok * k);
             if (w_out) memcpy(w_out, w, sizeof(double) * (size_t)ntok * k);
+            if (o_out) memcpy(o_out, o, sizeof(double) * (size_t)ntok * k * H);
         }
     }
     free(xs);

@@ -1,0 +1,130 @@
+"""GPU edge cases against the oracle: ragged and odd shapes, the extreme
+supported sizes, degenerate routing (E=1, k=E, exact ties), empty input, and
+guard canaries around every output."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_ffn_05_amd as moe
+import oracle
+import synth
+from tests.gpu_layer import GpuLayer, bf16_dev_to_f64, rel_err
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-2
+PATHS = [moe.MOE_PATH_SKINNY, moe.MOE_PATH_TILED]
+
+
+def _layer(T, H, E, k, I, wfmt=0, seed=3, zipf=0.0):
+    cfg = synth.LayerConfig(f"edge_T{T}_H{H}_E{E}_k{k}_I{I}", T=T, H=H, E=E, k=k, I=I, wfmt=wfmt, seed=seed,
+                            zipf_s=zipf)
+    return synth.make_layer(cfg)
+
+
+def _check_forward(layer, path):
+    c = layer.cfg
+    print(f"[edge] {c.name} wfmt={c.wfmt} path={path}", flush=True)
+    orc = oracle.get()
+    tokens = np.arange(c.T, dtype=np.int32)
+    y_ref, idx_ref, w_ref = orc.forward_tokens(layer.x, layer.w_router, layer.weights, c.k, c.I, tokens)
+    g = GpuLayer(layer, path)
+    g.forward()
+    torch.cuda.synchronize()
+    assert np.array_equal(g.topk_idx.cpu().numpy(), idx_ref)
+    assert np.max(np.abs(g.topk_w.cpu().numpy() - w_ref)) <= 1e-5
+    e = rel_err(bf16_dev_to_f64(g.y), y_ref)
+    assert e <= TOL, e
+    # the stage-by-stage chain gives the same bits as the fused entry point
+    y_fwd = g.y.clone()
+    g.stages()
+    torch.cuda.synchronize()
+    assert torch.equal(y_fwd, g.y)
+
+
+@pytest.mark.parametrize("path", PATHS, ids=["skinny", "tiled"])
+@pytest.mark.parametrize("shape", [(37, 96, 5, 2, 160), (100, 64, 3, 3, 96), (1, 32, 8, 2, 32), (130, 160, 16, 4, 224)],
+                         ids=lambda s: "T{}_H{}_E{}_k{}_I{}".format(*s))
+@pytest.mark.parametrize("wfmt", [0, 1], ids=["bf16", "mxfp4"])
+def test_ragged_shapes(shape, path, wfmt):
+    _check_forward(_layer(*shape, wfmt=wfmt), path)
+
+
+@pytest.mark.parametrize("path", PATHS, ids=["skinny", "tiled"])
+def test_single_expert_dense(path):
+    _check_forward(_layer(24, 64, 1, 1, 96), path)
+
+
+@pytest.mark.parametrize("path", PATHS, ids=["skinny", "tiled"])
+def test_k_equals_E(path):
+    _check_forward(_layer(19, 64, 4, 4, 64), path)
+
+
+@pytest.mark.parametrize("path", PATHS, ids=["skinny", "tiled"])
+def test_max_experts_and_k(path):
+    _check_forward(_layer(40, 64, 256, 8, 64), path)
+
+
+def test_skewed_prefill_small():
+    _check_forward(_layer(700, 64, 32, 4, 64, zipf=1.1), moe.MOE_PATH_TILED)
+
+
+def test_exact_ties_go_to_lower_index():
+    layer = _layer(16, 64, 8, 3, 64)
+    wr = layer.w_router.copy()
+    wr[6] = wr[1]
+    wr[3] = wr[1]  # experts 1, 3 and 6 always tie
+    layer = synth.Layer(layer.cfg, layer.x, wr, layer.weights)
+    _, idx_ref, _ = oracle.get().route(layer.x, wr, 3)
+    g = GpuLayer(layer)
+    g.route()
+    torch.cuda.synchronize()
+    idx = g.topk_idx.cpu().numpy()
+    assert np.array_equal(idx, idx_ref)
+    for t in range(16):
+        tied = [e for e in idx[t] if e in (1, 3, 6)]
+        assert tied == sorted(tied)
+
+
+def test_empty_batch_is_noop():
+    layer = _layer(4, 64, 4, 2, 64)
+    g = GpuLayer(layer)
+    d0 = moe.dims(0, 64, 4, 2, 64)
+    g.y.fill_(7)
+    moe.moe_forward(d0, g.x, g.w_router, g.weights, g.y, None, None, g.ws, g.ws_bytes)
+    moe.moe_route(d0, g.x, g.w_router, g.topk_idx, g.topk_w, g.ws, g.ws_bytes)
+    torch.cuda.synchronize()
+    assert bool((g.y == 7).all())
+
+
+def test_guard_canaries():
+    """Outputs sit inside 4 KiB guard bands of 0xA5; no kernel writes outside."""
+    layer = _layer(33, 96, 6, 2, 128)
+    c = layer.cfg
+    g = GpuLayer(layer)
+    guard = 4096
+
+    def guarded(nbytes):
+        buf = torch.full((nbytes + 2 * guard,), 0xA5, dtype=torch.uint8, device="cuda")
+        return buf, buf[guard:guard + nbytes]
+
+    P = c.T * c.k
+    bufs = {n: guarded(b) for n, b in dict(y=c.T * c.H * 2, idx=P * 4, w=P * 4, off=(c.E + 1) * 4, sp=P * 4,
+                                           pr=P * 4, h=P * c.I * 2, ys=P * c.H * 2).items()}
+    v = {n: b[1] for n, b in bufs.items()}
+    for path in PATHS:
+        g.set_path(path)
+        moe.moe_route(g.dims, g.x, g.w_router, v["idx"], v["w"], g.ws, g.ws_bytes)
+        moe.moe_permute(g.dims, v["idx"], v["off"], v["sp"], v["pr"], g.ws, g.ws_bytes)
+        moe.moe_gate_up(g.dims, g.x, v["off"], v["sp"], g.weights, v["h"], g.ws, g.ws_bytes)
+        moe.moe_down(g.dims, v["h"], v["off"], g.weights, v["ys"], g.ws, g.ws_bytes)
+        moe.moe_combine(g.dims, v["ys"], v["pr"], v["w"], v["y"])
+        moe.moe_forward(g.dims, g.x, g.w_router, g.weights, v["y"], v["idx"], v["w"], g.ws, g.ws_bytes)
+    torch.cuda.synchronize()
+    for n, (buf, _) in bufs.items():
+        assert bool((buf[:guard] == 0xA5).all()) and bool((buf[-guard:] == 0xA5).all()), f"guard of {n} overwritten"
+    y_ref, _, _ = oracle.get().forward_tokens(layer.x, layer.w_router, layer.weights, c.k, c.I, np.arange(c.T))
+    y = synth.f32_from_bf16(v["y"].cpu().numpy().view(np.uint16)).astype(np.float64).reshape(c.T, c.H)
+    assert rel_err(y, y_ref) <= TOL
