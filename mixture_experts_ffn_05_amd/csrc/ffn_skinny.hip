@@ -96,6 +96,7 @@ __global__ __launch_bounds__(SK_WAVES * WAVE) void gate_up_skinny_kernel(FfnArgs
                 accg = mfma16(as_bf16x8(wg[q]), as_bf16x8(xb[q]), accg);
                 accu = mfma16(as_bf16x8(wu[q]), as_bf16x8(xb[q]), accu);
             }
+            if (kk + SK_KSTEP >= H) mfma_drain();
         }
         if (tv) {
             // lane holds rows n0 + 4g .. +3 (gate and up alike) of token column r
@@ -135,6 +136,7 @@ __global__ __launch_bounds__(SK_WAVES * WAVE) void down_skinny_kernel(FfnArgs a)
             load_a32(hrow, kofs, kv && tv, hb);
 #pragma unroll
             for (int q = 0; q < 4; ++q) acc = mfma16(as_bf16x8(wv[q]), as_bf16x8(hb[q]), acc);
+            if (kk + SK_KSTEP >= I) mfma_drain();
         }
         if (tv) {
             uint2 o;

@@ -124,6 +124,7 @@ __global__ __launch_bounds__(TL_THREADS) void gate_up_tiled_kernel(FfnArgs a)
         stage_acts(H, kk, arow, Xs);
         __syncthreads();
         tile_mma(Ws, Xs, acc);
+        if (kk + TL_BK >= H) mfma_drain();
         __syncthreads();
     }
     // acc[0..1]: gate rows 0-15, 16-31; acc[2..3]: the matching up rows
@@ -170,6 +171,7 @@ __global__ __launch_bounds__(TL_THREADS) void down_tiled_kernel(FfnArgs a)
         stage_acts(I, kk, arow, Xs);
         __syncthreads();
         tile_mma(Ws, Xs, acc);
+        if (kk + TL_BK >= I) mfma_drain();
         __syncthreads();
     }
     const int lane = lane_id(), wave = threadIdx.x / WAVE;

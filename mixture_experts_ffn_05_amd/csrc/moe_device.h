@@ -45,6 +45,21 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c)
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// Idle cycles between the last MFMA of a K loop and the first read of its
+// accumulator.  hipcc's hazard recognizer was seen to place no wait states
+// before the first accumulator read in the block after a K loop
+// (v_mfma_f32_16x16x32_bf16 on gfx950), so the read returned a stale partial
+// sum.  Call it as the last statement of the loop body on the final
+// iteration (the accumulator copies are materialised in the loop's exit
+// block, after it).  20 wait states cover the 8-pass MFMA; the scheduling
+// barriers keep the MFMAs from sinking below them.
+__device__ __forceinline__ void mfma_drain()
+{
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 // --------------------------------------------------------------- MXFP4
 // Dequantise 8 E2M1 values (one 32-bit word, element 2i in the low nibble of
 // byte i) times the block scale into 8 bf16 (exact: a power-of-two scale
