@@ -123,8 +123,14 @@ moe::FfnArgs ffn_args(const moe_dims& d)
 
 // ---- stage bodies (arguments already validated) ----
 
+// Up to this many tokens the router runs as one kernel, a workgroup per token.
+constexpr int kRouteSmallMaxT = 256;
+
 int do_route(const moe_dims& d, const void* x, const void* wr, int32_t* idx, float* w, void* ws, hipStream_t s)
 {
+    if (d.T <= kRouteSmallMaxT)
+        return hip_status(moe::launch_router_small(d.T, d.H, d.E, d.k, static_cast<const uint16_t*>(x),
+                                                   static_cast<const uint16_t*>(wr), idx, w, s));
     const Layout L = layout_for(d);
     double* logits = region<double>(ws, L.logits);
     int rc = hip_status(moe::launch_router_logits_f64(d.T, d.H, d.E, static_cast<const uint16_t*>(x),

@@ -17,6 +17,9 @@ hipError_t launch_router_logits_f64(int T, int H, int E, const uint16_t* x, cons
 // Top-k by logit (ties -> lower index) + softmax over the k, one wave per token.
 hipError_t launch_router_select(int T, int E, int k, const double* logits, int32_t* topk_idx, float* topk_w,
                                 hipStream_t s);
+// Small batches: logits + selection in one kernel, one workgroup per token.
+hipError_t launch_router_small(int T, int H, int E, int k, const uint16_t* x, const uint16_t* wr, int32_t* topk_idx,
+                               float* topk_w, hipStream_t s);
 
 // ------------------------------------------------------------------ permute
 constexpr int PERMUTE_CHUNK = 1024;  // pairs ranked per workgroup pass
