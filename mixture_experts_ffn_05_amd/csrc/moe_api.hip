@@ -123,20 +123,33 @@ moe::FfnArgs ffn_args(const moe_dims& d)
 
 // ---- stage bodies (arguments already validated) ----
 
-// Up to this many tokens the router runs as one kernel, a workgroup per token.
-constexpr int kRouteSmallMaxT = 256;
-
 int do_route(const moe_dims& d, const void* x, const void* wr, int32_t* idx, float* w, void* ws, hipStream_t s)
 {
-    if (d.T <= kRouteSmallMaxT)
-        return hip_status(moe::launch_router_small(d.T, d.H, d.E, d.k, static_cast<const uint16_t*>(x),
-                                                   static_cast<const uint16_t*>(wr), idx, w, s));
     const Layout L = layout_for(d);
     double* logits = region<double>(ws, L.logits);
     int rc = hip_status(moe::launch_router_logits_f64(d.T, d.H, d.E, static_cast<const uint16_t*>(x),
                                                       static_cast<const uint16_t*>(wr), logits, s));
     if (rc) return rc;
     return hip_status(moe::launch_router_select(d.T, d.E, d.k, logits, idx, w, s));
+}
+
+// Route + permute.  When one workgroup can permute all pairs, selection and
+// permutation run as one kernel after the logits kernel.
+int do_route_permute(const moe_dims& d, const void* x, const void* wr, int32_t* idx, float* w, int32_t* off,
+                     int32_t* sp, int32_t* pr, void* ws, hipStream_t s)
+{
+    if (!moe::permute_fits_one_block(d.T * d.k)) {
+        int rc = do_route(d, x, wr, idx, w, ws, s);
+        if (rc) return rc;
+        const Layout L = layout_for(d);
+        return hip_status(moe::launch_permute(d.T * d.k, d.E, idx, off, sp, pr, region<void>(ws, L.perm_scratch), s));
+    }
+    const Layout L = layout_for(d);
+    double* logits = region<double>(ws, L.logits);
+    int rc = hip_status(moe::launch_router_logits_f64(d.T, d.H, d.E, static_cast<const uint16_t*>(x),
+                                                      static_cast<const uint16_t*>(wr), logits, s));
+    if (rc) return rc;
+    return hip_status(moe::launch_select_permute_small(d.T, d.E, d.k, logits, idx, w, off, sp, pr, s));
 }
 
 int do_permute(const moe_dims& d, const int32_t* idx, int32_t* off, int32_t* sp, int32_t* pr, void* ws, hipStream_t s)
@@ -292,8 +305,7 @@ int moe_forward(const moe_dims* dims, const void* x, const void* w_router, const
     int32_t* pr = region<int32_t>(workspace, L.rank);
     void* h = region<void>(workspace, L.h);
     void* ys = region<void>(workspace, L.y_sorted);
-    if ((rc = do_route(d, x, w_router, idx, w, workspace, s))) return rc;
-    if ((rc = do_permute(d, idx, off, sp, pr, workspace, s))) return rc;
+    if ((rc = do_route_permute(d, x, w_router, idx, w, off, sp, pr, workspace, s))) return rc;
     if ((rc = do_gate_up(d, x, off, sp, *weights, h, s))) return rc;
     if ((rc = do_down(d, h, off, *weights, ys, s))) return rc;
     return hip_status(moe::launch_combine(d.T, d.H, d.k, static_cast<const uint16_t*>(ys), pr, w,

@@ -158,4 +158,74 @@ __device__ __forceinline__ int locate_m_tile(const int32_t* __restrict__ offsets
     return -1;
 }
 
+// --------------------------------------------------------------- routing
+// Selection rule (the pages give top-k routing without a tie rule; the reading
+// taken is): larger logit first, an exactly equal logit goes to the lower
+// expert index; weights = softmax over the k selected logits.
+
+// Does candidate (v, i) rank before (bv, bi)?  Larger logit first, then the
+// lower expert index.
+__device__ __forceinline__ bool ranks_before(double v, int i, double bv, int bi)
+{
+    return v > bv || (v == bv && i < bi);
+}
+
+// Top-k of one token's E logits (row: global or LDS) by one wave: k rounds of
+// a wave-wide arg-max (each lane owns experts lane, lane+64, ...), then the
+// softmax over the k selected.  Lane j writes slot j.
+__device__ __forceinline__ void wave_topk_softmax(const double* row, int E, int k, int32_t* __restrict__ idx_out,
+                                  float* __restrict__ w_out)
+{
+    const int lane = lane_id();
+    double v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int e = lane + WAVE * i;
+        v[i] = e < E ? row[e] : -__builtin_inf();
+    }
+    uint32_t taken = 0;
+    double sel_v[8];
+    int sel_i[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        sel_v[j] = 0.0;
+        sel_i[j] = 0;
+        if (j < k) {
+            double bv = -__builtin_inf();
+            int bi = 0x7FFFFFFF;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int e = lane + WAVE * i;
+                if (e < E && !(taken >> i & 1u) && ranks_before(v[i], e, bv, bi)) {
+                    bv = v[i];
+                    bi = e;
+                }
+            }
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) {
+                const double ov = __shfl_xor(bv, o, WAVE);
+                const int oi = __shfl_xor(bi, o, WAVE);
+                if (ranks_before(ov, oi, bv, bi)) {
+                    bv = ov;
+                    bi = oi;
+                }
+            }
+            sel_v[j] = bv;
+            sel_i[j] = bi;
+            if ((bi & (WAVE - 1)) == lane) taken |= 1u << (bi / WAVE);
+        }
+    }
+    double z = 0.0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        if (j < k) z += exp(sel_v[j] - sel_v[0]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        if (j < k && lane == j) {
+            idx_out[j] = sel_i[j];
+            w_out[j] = (float)(exp(sel_v[j] - sel_v[0]) / z);
+        }
+    }
+}
+
 }  // namespace moe

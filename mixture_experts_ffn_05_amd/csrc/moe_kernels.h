@@ -17,9 +17,7 @@ hipError_t launch_router_logits_f64(int T, int H, int E, const uint16_t* x, cons
 // Top-k by logit (ties -> lower index) + softmax over the k, one wave per token.
 hipError_t launch_router_select(int T, int E, int k, const double* logits, int32_t* topk_idx, float* topk_w,
                                 hipStream_t s);
-// Small batches: logits + selection in one kernel, one workgroup per token.
-hipError_t launch_router_small(int T, int H, int E, int k, const uint16_t* x, const uint16_t* wr, int32_t* topk_idx,
-                               float* topk_w, hipStream_t s);
+
 
 // ------------------------------------------------------------------ permute
 constexpr int PERMUTE_CHUNK = 1024;  // pairs ranked per workgroup pass
@@ -27,6 +25,12 @@ constexpr int PERMUTE_CHUNK = 1024;  // pairs ranked per workgroup pass
 size_t permute_scratch_bytes(int64_t P, int E);
 hipError_t launch_permute(int P, int E, const int32_t* topk_idx, int32_t* offsets, int32_t* sorted_pairs,
                           int32_t* pair_rank, void* scratch, hipStream_t s);
+// True when one workgroup permutes all P pairs (then selection can be fused in).
+bool permute_fits_one_block(int P);
+// Top-k selection of all T tokens from logits [T][E] followed by the
+// permutation, in one workgroup (requires permute_fits_one_block(T*k)).
+hipError_t launch_select_permute_small(int T, int E, int k, const double* logits, int32_t* topk_idx, float* topk_w,
+                                       int32_t* offsets, int32_t* sorted_pairs, int32_t* pair_rank, hipStream_t s);
 
 // ------------------------------------------------------------------ expert FFN
 struct FfnArgs {

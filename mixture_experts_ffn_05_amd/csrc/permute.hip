@@ -71,10 +71,10 @@ __device__ void scan_counts_wave0(int* counts, int E, int32_t* offsets)
     if (lane == 0) offsets[E] = run;
 }
 
-__global__ __launch_bounds__(PB_THREADS) void permute_small_kernel(int P, int E, const int32_t* __restrict__ topk_idx,
-                                                                    int32_t* __restrict__ offsets,
-                                                                    int32_t* __restrict__ sorted_pairs,
-                                                                    int32_t* __restrict__ pair_rank)
+// Whole permutation of P <= SMALL_P pairs by one workgroup of PB_THREADS:
+// histogram, exclusive scan, then the stable scatter in passes of 1024 pairs.
+__device__ void permute_block(int P, int E, const int32_t* __restrict__ topk_idx, int32_t* __restrict__ offsets,
+                              int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ pair_rank)
 {
     __shared__ int wave_counts[PB_WAVES * MAX_E];
     __shared__ int chunk_total[MAX_E];
@@ -103,6 +103,27 @@ __global__ __launch_bounds__(PB_THREADS) void permute_small_kernel(int P, int E,
     }
 }
 
+__global__ __launch_bounds__(PB_THREADS) void permute_small_kernel(int P, int E, const int32_t* __restrict__ topk_idx,
+                                                                    int32_t* __restrict__ offsets,
+                                                                    int32_t* __restrict__ sorted_pairs,
+                                                                    int32_t* __restrict__ pair_rank)
+{
+    permute_block(P, E, topk_idx, offsets, sorted_pairs, pair_rank);
+}
+
+// Small batches: top-k selection of every token (one wave per token, logits
+// [T][E] from the router) followed by the permutation, in one workgroup.
+__global__ __launch_bounds__(PB_THREADS) void select_permute_small_kernel(
+    int T, int E, int k, const double* __restrict__ logits, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_w, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs,
+    int32_t* __restrict__ pair_rank)
+{
+    for (int t = threadIdx.x / WAVE; t < T; t += PB_WAVES)
+        wave_topk_softmax(logits + (size_t)t * E, E, k, topk_idx + (size_t)t * k, topk_w + (size_t)t * k);
+    __syncthreads();  // this workgroup's topk_idx stores are visible to it after the barrier
+    permute_block(T * k, E, topk_idx, offsets, sorted_pairs, pair_rank);
+}
+
 // Pass 1 of the multi-block path: chunk b = blockIdx.x ranks its pairs and
 // writes rank[p] and hist[b][e].
 __global__ __launch_bounds__(PB_THREADS) void permute_count_kernel(int P, int E, const int32_t* __restrict__ topk_idx,
@@ -120,28 +141,29 @@ __global__ __launch_bounds__(PB_THREADS) void permute_count_kernel(int P, int E,
     for (int e = threadIdx.x; e < E; e += blockDim.x) hist[(size_t)blockIdx.x * E + e] = chunk_total[e];
 }
 
-// Pass 2: per expert, the exclusive prefix over chunks; then the expert
-// offsets; hist[b][e] becomes the global base of chunk b inside expert e.
-__global__ __launch_bounds__(256) void permute_scan_kernel(int nchunks, int E, int32_t* __restrict__ hist,
-                                                           int32_t* __restrict__ offsets)
+// Pass 2: per expert (one wave each), the exclusive prefix over chunks; then
+// the expert offsets; hist[b][e] becomes the global base of chunk b inside
+// expert e.
+__global__ __launch_bounds__(PB_THREADS) void permute_scan_kernel(int nchunks, int E, int32_t* __restrict__ hist,
+                                                                  int32_t* __restrict__ offsets)
 {
     __shared__ int totals[MAX_E];
-    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    const int wave = threadIdx.x / WAVE, lane = lane_id();
+    for (int e = wave; e < E; e += PB_WAVES) {
         int run = 0;
-        for (int b = 0; b < nchunks; ++b) {
-            const int c = hist[(size_t)b * E + e];
-            hist[(size_t)b * E + e] = run;
-            run += c;
+        for (int b0 = 0; b0 < nchunks; b0 += WAVE) {
+            const int b = b0 + lane;
+            const int c = b < nchunks ? hist[(size_t)b * E + e] : 0;
+            const int ex = wave_excl_scan(c) + run;
+            if (b < nchunks) hist[(size_t)b * E + e] = ex;
+            run = __shfl(ex + c, WAVE - 1, WAVE);
         }
-        totals[e] = run;
+        if (lane == 0) totals[e] = run;
     }
     __syncthreads();
     scan_counts_wave0(totals, E, offsets);
     __syncthreads();
-    for (int e = threadIdx.x; e < E; e += blockDim.x) {
-        const int base = totals[e];
-        for (int b = 0; b < nchunks; ++b) hist[(size_t)b * E + e] += base;
-    }
+    for (int i = threadIdx.x; i < nchunks * E; i += blockDim.x) hist[i] += totals[i % E];
 }
 
 // Pass 3: scatter.
@@ -157,6 +179,16 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(int P, int E, cons
     const int s = hist[(size_t)(p / PB_THREADS) * E + e] + rank[p];
     sorted_pairs[s] = p;
     pair_rank[p] = s;
+}
+
+bool permute_fits_one_block(int P) { return P <= SMALL_P; }
+
+hipError_t launch_select_permute_small(int T, int E, int k, const double* logits, int32_t* topk_idx, float* topk_w,
+                                       int32_t* offsets, int32_t* sorted_pairs, int32_t* pair_rank, hipStream_t s)
+{
+    hipLaunchKernelGGL(select_permute_small_kernel, dim3(1), dim3(PB_THREADS), 0, s, T, E, k, logits, topk_idx,
+                       topk_w, offsets, sorted_pairs, pair_rank);
+    return hipGetLastError();
 }
 
 size_t permute_scratch_bytes(int64_t P, int E)
@@ -179,7 +211,7 @@ hipError_t launch_permute(int P, int E, const int32_t* topk_idx, int32_t* offset
     hipLaunchKernelGGL(permute_count_kernel, dim3(nchunks), dim3(PB_THREADS), 0, s, P, E, topk_idx, rank, hist);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(256), 0, s, nchunks, E, hist, offsets);
+    hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(PB_THREADS), 0, s, nchunks, E, hist, offsets);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(permute_scatter_kernel, dim3((P + 255) / 256), dim3(256), 0, s, P, E, topk_idx, rank, hist,
