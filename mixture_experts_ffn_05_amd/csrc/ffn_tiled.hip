@@ -1,216 +1,411 @@
 // Tiled grouped expert GEMM (prefill regime): many tokens per expert.
 //
 // Each expert segment of the permutation is an independent GEMM
-//   gate/up: [M_e tokens] x [2I weight rows], K = H, A rows gathered from x
-//   down:    [M_e rows of h] x [H weight rows], K = I
-// with fp32 accumulation on bf16 MFMA (v_mfma_f32_16x16x32_bf16).  MXFP4
+//   gate/up: [2I weight rows] x [M_e tokens], K = H, token rows gathered from x
+//   down:    [H weight rows]  x [M_e rows of h], K = I
+// with fp32 accumulation on bf16 MFMA (v_mfma_f32_32x32x16_bf16).  MXFP4
 // weights (Persona Kappa post, section "Quantization-Aware Training (QAT)":
 // W4A16, activations stay bf16) are decoded to bf16 while being staged into
-// LDS.  The gate/up kernel computes gate and up rows of the same output
-// columns in one tile and applies silu(gate)*up before writing h.
+// LDS.  The gate/up kernel holds gate and up rows of the same output columns
+// in one tile and applies silu(gate)*up in registers before writing h.
 //
-// Schedule: grid.y enumerates the M-tiles of all experts (expert e owns
-// ceil(M_e/BM) consecutive ones; the grid is sized for the worst case
-// P/BM + E and surplus blocks exit), grid.x the N-tiles.
+// Tile: 256 weight rows x 256 tokens, 4 waves in 2 x 2; a wave owns 128
+// weight rows x 128 tokens = 4 x 4 blocks of 32x32 in 256 accumulator
+// registers, so per 16-wide K step it reads 8 operand fragments from LDS for
+// 16 MFMAs (the next step's fragments are read while the current MFMAs run).
+// For gate/up the tile's weight rows are ordered [g0 g1 u0 u1 | g2 g3 u2 u3]
+// (32-row blocks of gate and up rows of the same 128 output columns), so each
+// wave holds matching gate and up blocks.
+//
+// K advances in stages of 32 (the C-ABI admits only hidden and expert widths
+// that are multiples of 32, so there is no K tail) through a ring of 4 LDS
+// buffers: bf16 operands
+// are loaded straight into LDS with global_load_lds three stages ahead of the
+// MFMAs (no staging registers), so each stage's loads have three stages of
+// MFMAs to land; MXFP4 weights take a register detour two stages ahead to be
+// decoded.  One barrier per stage, placed after the stage's first 16 MFMAs
+// are issued so the matrix pipe stays busy through it.  LDS rows are 64 B (32 bf16) with 16-B
+// chunks XOR-swizzled by (row/4)%4, so the 16 lanes that read one chunk of 16
+// consecutive rows hit 16 distinct bank groups.
+//
+// Schedule: the grid enumerates tiles in bands of 4 M-tiles per expert, the
+// 4 M-tiles of one N-tile adjacent, so neighbouring tiles share token rows or
+// weight rows; block b works on tile (b % 8) * ceil(tiles / 8) + b / 8 so that
+// the blocks resident on one XCD (dispatched round-robin by block index) take
+// a contiguous run of tiles and share its L2.
+#include <type_traits>
+
 #include "moe_device.h"
 #include "moe_kernels.h"
 
 namespace moe {
 
-constexpr int TL_BM = 64;       // tokens per tile
-constexpr int TL_BW = 64;       // weight rows per tile (gate/up: 32 gate + 32 up)
-constexpr int TL_BK = 128;      // K per stage
-constexpr int TL_LD = TL_BK + 8;  // LDS row stride in bf16 (pad 16 B: conflict-free 16-B reads)
-constexpr int TL_THREADS = 256;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
 
-// Stage 64 weight rows x 128 K of bf16 or MXFP4 (decoded) into Ws.
-// rowof(i) gives the global row index of tile row i, or -1 for none.
-template <int WFMT, typename RowOf>
-__device__ __forceinline__ void stage_weights(const void* __restrict__ w, const uint8_t* __restrict__ wsc, int K,
-                                              int kk, RowOf rowof, uint16_t* Ws)
+constexpr int GM_THREADS = 256;
+constexpr int GM_BT = 256;    // tokens per tile (MFMA N side)
+constexpr int GM_BW = 256;    // weight rows per tile (MFMA M side)
+constexpr int GM_BK = 32;     // K per stage
+constexpr int GM_NBUF = 4;    // LDS stages
+constexpr int GM_DIST = 3;    // bf16 loads run this many stages ahead
+constexpr int GM_WB = 4;      // weight blocks per wave (128 rows)
+constexpr int GM_TB = 4;      // token blocks per wave (128 tokens)
+constexpr int GM_BAND = 4;    // M-tiles per band
+constexpr int GM_ROWB = GM_BK * 2;                                   // bytes per LDS row (64)
+constexpr int GM_DL = GM_BW * GM_ROWB / 1024 / (GM_THREADS / WAVE);  // direct loads per wave per operand (4)
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c)
 {
-    if constexpr (WFMT == 0) {
-        // 64 rows x 16 chunks of 8 elements; 4 chunks per thread
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int c = threadIdx.x + TL_THREADS * q;
-            const int i = c >> 4, part = c & 15;
-            const long long row = rowof(i);
-            const int k = kk + part * 8;
-            u32x4 v = {0, 0, 0, 0};
-            if (row >= 0 && k < K) v = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(w) + row * K + k);
-            *reinterpret_cast<u32x4*>(Ws + i * TL_LD + part * 8) = v;
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Byte offset of 16-B chunk c (0..3) of row r in a [rows][32] bf16 LDS tile.
+__device__ __forceinline__ int gm_swz(int r, int c) { return r * GM_ROWB + ((c ^ ((r >> 2) & 3)) << 4); }
+
+// Wait until at most n vector-memory operations of this wave are outstanding.
+template <int n>
+__device__ __forceinline__ void vm_wait()
+{
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier after this wave's LDS writes have completed.  It carries
+// no memory fence: the direct-to-LDS loads still in flight belong to later
+// stages and are waited for explicitly (vm_wait), and a fence here would make
+// the compiler drain them.  The asm memory clobber keeps the compiler from
+// moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+struct GmShared {
+    uint8_t w[GM_NBUF][GM_BW * GM_ROWB];
+    uint8_t x[GM_NBUF][GM_BT * GM_ROWB];
+};
+
+// Which expert and local tile a linear tile index belongs to.  Expert e owns
+// ceil(M_e / BT) * nt consecutive tiles.  One wave; returns -1 past the end.
+__device__ __forceinline__ int gm_locate(const int32_t* __restrict__ offsets, int E, int nt, int tile, int* local,
+                                         int* mtiles)
+{
+    const int lane = lane_id();
+    int before = 0;
+    for (int base = 0; base < E; base += WAVE) {
+        const int e = base + lane;
+        int mt = 0;
+        if (e < E) mt = (offsets[e + 1] - offsets[e] + GM_BT - 1) / GM_BT;
+        const int n = mt * nt;
+        const int excl = wave_excl_scan(n) + before;
+        const uint64_t hm = ballot(n > 0 && tile >= excl && tile < excl + n);
+        if (hm) {
+            const int src = (int)__builtin_ctzll(hm);
+            *local = tile - __shfl(excl, src, WAVE);
+            *mtiles = __shfl(mt, src, WAVE);
+            return base + src;
         }
+        before = __shfl(excl + n, WAVE - 1, WAVE);
+    }
+    return -1;
+}
+
+__device__ __forceinline__ int gm_total_tiles(const int32_t* __restrict__ offsets, int E, int nt)
+{
+    int n = 0;
+    for (int base = 0; base < E; base += WAVE) {
+        const int e = base + lane_id();
+        const int mt = e < E ? (offsets[e + 1] - offsets[e] + GM_BT - 1) / GM_BT : 0;
+        n += wave_sum(mt);
+    }
+    return n * nt;
+}
+
+// Local tile -> (m-tile, n-tile): bands of GM_BAND m-tiles; inside a band the
+// m-tiles of one n-tile are adjacent, then the next n-tile.
+__device__ __forceinline__ void gm_band(int local, int mtiles, int nt, int* m, int* n)
+{
+    const int full = mtiles / GM_BAND;
+    if (local < full * GM_BAND * nt) {
+        const int band = local / (GM_BAND * nt), rem = local % (GM_BAND * nt);
+        *n = rem / GM_BAND;
+        *m = band * GM_BAND + rem % GM_BAND;
     } else {
-        // 64 rows x 4 blocks of 32 elements (16 bytes + 1 scale); 1 block per thread
-        const int i = threadIdx.x >> 2, part = threadIdx.x & 3;
-        const long long row = rowof(i);
-        const int k = kk + part * 32;
-        u32x4 d[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
-        if (row >= 0 && k < K) {
-            const u32x4 qv =
-                *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(w) + row * (K / 2) + k / 2);
-            const float sc = e8m0_to_f32(wsc[row * (K / 32) + k / 32]);
-            d[0] = fp4x8_to_bf16x8(qv.x, sc);
-            d[1] = fp4x8_to_bf16x8(qv.y, sc);
-            d[2] = fp4x8_to_bf16x8(qv.z, sc);
-            d[3] = fp4x8_to_bf16x8(qv.w, sc);
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) *reinterpret_cast<u32x4*>(Ws + i * TL_LD + part * 32 + q * 8) = d[q];
+        const int rem = local - full * GM_BAND * nt, bm = mtiles - full * GM_BAND;
+        *n = rem / bm;
+        *m = full * GM_BAND + rem % bm;
     }
 }
 
-// Stage 64 activation rows x 128 K (bf16) into Xs; arow(i) = row pointer or null.
-template <typename ARow>
-__device__ __forceinline__ void stage_acts(int K, int kk, ARow arow, uint16_t* Xs)
+// Global weight row of tile row i, or -1 past the output width.  gate/up:
+// 32-row block b = i/32 holds gate (b%4 < 2) or up rows of output columns
+// 64*(b/4) + 32*(b%2) + i%32 of the tile.
+template <bool GATE_UP>
+__device__ __forceinline__ long long gm_wrow(const FfnArgs& a, int e, int n0, int NOUT, int i)
 {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int c = threadIdx.x + TL_THREADS * q;
-        const int i = c >> 4, part = c & 15;
-        const uint16_t* p = arow(i);
-        const int k = kk + part * 8;
-        u32x4 v = {0, 0, 0, 0};
-        if (p && k < K) v = *reinterpret_cast<const u32x4*>(p + k);
-        *reinterpret_cast<u32x4*>(Xs + i * TL_LD + part * 8) = v;
-    }
-}
-
-// One stage of MFMAs: wave w owns tokens 16w..16w+15 and all 4 weight-row
-// tiles of 16.
-__device__ __forceinline__ void tile_mma(const uint16_t* Ws, const uint16_t* Xs, f32x4 acc[4])
-{
-    const int lane = lane_id(), wave = threadIdx.x / WAVE;
-    const int r = lane & 15, g = lane >> 4;
-#pragma unroll
-    for (int q = 0; q < TL_BK / 32; ++q) {
-        const bf16x8 b = as_bf16x8(*reinterpret_cast<const u32x4*>(Xs + (16 * wave + r) * TL_LD + 32 * q + 8 * g));
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const bf16x8 av = as_bf16x8(*reinterpret_cast<const u32x4*>(Ws + (16 * m + r) * TL_LD + 32 * q + 8 * g));
-            acc[m] = mfma16(av, b, acc[m]);
-        }
-    }
-}
-
-template <int WFMT>
-__global__ __launch_bounds__(TL_THREADS) void gate_up_tiled_kernel(FfnArgs a)
-{
-    __shared__ __attribute__((aligned(16))) uint16_t Ws[TL_BW * TL_LD];
-    __shared__ __attribute__((aligned(16))) uint16_t Xs[TL_BM * TL_LD];
-    __shared__ int tok[TL_BM];
-    int mt;
-    const int e = locate_m_tile(a.offsets, a.E, TL_BM, blockIdx.y, &mt);
-    if (e < 0) return;  // uniform per block
-    const int H = a.H, I = a.I;
-    const int n0 = blockIdx.x * (TL_BW / 2);  // first output column (gate row)
-    const int seg0 = a.offsets[e], seg1 = a.offsets[e + 1];
-    const int sbase = seg0 + mt * TL_BM;
-    if (threadIdx.x < TL_BM) {
-        const int s = sbase + threadIdx.x;
-        tok[threadIdx.x] = s < seg1 ? a.sorted_pairs[s] / a.k : -1;
-    }
-    __syncthreads();
-    auto rowof = [&](int i) -> long long {
-        const int n = n0 + (i & 31);
-        if (n >= I) return -1;
-        return (long long)e * 2 * I + (i < 32 ? n : I + n);
-    };
-    auto arow = [&](int i) -> const uint16_t* { return tok[i] >= 0 ? a.x + (size_t)tok[i] * H : nullptr; };
-    f32x4 acc[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
-    for (int kk = 0; kk < H; kk += TL_BK) {
-        stage_weights<WFMT>(a.w, a.w_scale, H, kk, rowof, Ws);
-        stage_acts(H, kk, arow, Xs);
-        __syncthreads();
-        tile_mma(Ws, Xs, acc);
-        if (kk + TL_BK >= H) mfma_drain();
-        __syncthreads();
-    }
-    // acc[0..1]: gate rows 0-15, 16-31; acc[2..3]: the matching up rows
-    const int lane = lane_id(), wave = threadIdx.x / WAVE;
-    const int r = lane & 15, g = lane >> 4;
-    const int s = sbase + 16 * wave + r;
-    if (s < seg1) {
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            const int n = n0 + 16 * m + 4 * g;
-            if (n < I) {
-                uint2 o;
-                o.x = pack_bf16x2(silu(acc[m][0]) * acc[m + 2][0], silu(acc[m][1]) * acc[m + 2][1]);
-                o.y = pack_bf16x2(silu(acc[m][2]) * acc[m + 2][2], silu(acc[m][3]) * acc[m + 2][3]);
-                *reinterpret_cast<uint2*>(a.out + (size_t)s * I + n) = o;
-            }
-        }
-    }
-}
-
-template <int WFMT>
-__global__ __launch_bounds__(TL_THREADS) void down_tiled_kernel(FfnArgs a)
-{
-    __shared__ __attribute__((aligned(16))) uint16_t Ws[TL_BW * TL_LD];
-    __shared__ __attribute__((aligned(16))) uint16_t Xs[TL_BM * TL_LD];
-    int mt;
-    const int e = locate_m_tile(a.offsets, a.E, TL_BM, blockIdx.y, &mt);
-    if (e < 0) return;
-    const int H = a.H, I = a.I;
-    const int n0 = blockIdx.x * TL_BW;
-    const int seg1 = a.offsets[e + 1];
-    const int sbase = a.offsets[e] + mt * TL_BM;
-    auto rowof = [&](int i) -> long long {
+    if constexpr (GATE_UP) {
+        const int b = i >> 5;
+        const int n = n0 + 64 * (b >> 2) + 32 * (b & 1) + (i & 31);
+        if (n >= NOUT) return -1;
+        return (long long)e * 2 * a.I + ((b & 2) ? a.I + n : n);
+    } else {
         const int n = n0 + i;
-        return n < H ? (long long)e * H + n : -1;
-    };
-    auto arow = [&](int i) -> const uint16_t* {
-        const int s = sbase + i;
-        return s < seg1 ? a.a_rows + (size_t)s * I : nullptr;
-    };
-    f32x4 acc[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
-    for (int kk = 0; kk < I; kk += TL_BK) {
-        stage_weights<WFMT>(a.w, a.w_scale, I, kk, rowof, Ws);
-        stage_acts(I, kk, arow, Xs);
-        __syncthreads();
-        tile_mma(Ws, Xs, acc);
-        if (kk + TL_BK >= I) mfma_drain();
-        __syncthreads();
+        return n < NOUT ? (long long)e * a.H + n : -1;
     }
-    const int lane = lane_id(), wave = threadIdx.x / WAVE;
-    const int r = lane & 15, g = lane >> 4;
-    const int s = sbase + 16 * wave + r;
-    if (s < seg1) {
+}
+
+template <int WFMT, bool GATE_UP>
+__global__ __launch_bounds__(GM_THREADS, 1) void gemm_kernel(FfnArgs a)
+{
+    __shared__ __attribute__((aligned(16))) GmShared sh;
+    const int NOUT = GATE_UP ? a.I : a.H;  // output columns
+    const int K = GATE_UP ? a.H : a.I;
+    const int WCOLS = GATE_UP ? GM_BW / 2 : GM_BW;  // output columns per tile
+    const int nt = (NOUT + WCOLS - 1) / WCOLS;
+
+    // ---- tile of this block
+    const int total = gm_total_tiles(a.offsets, a.E, nt);
+    const int per = (total + 7) / 8;
+    if ((int)blockIdx.x / 8 >= per) return;  // uniform per block
+    const int tile = (blockIdx.x % 8) * per + blockIdx.x / 8;
+    if (tile >= total) return;
+    int local, mtiles;
+    const int e = gm_locate(a.offsets, a.E, nt, tile, &local, &mtiles);
+    int mt, ntile;
+    gm_band(local, mtiles, nt, &mt, &ntile);
+    const int seg1 = a.offsets[e + 1];
+    const int sbase = a.offsets[e] + mt * GM_BT;
+    const int n0 = ntile * WCOLS;
+
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid / WAVE;
+    const int r32 = lane & 31, kg = lane >> 5;
+    const int wt = wave & 1, ww = wave >> 1;  // token half, weight half of this wave
+
+    // ---- direct-to-LDS staging of bf16 tiles.  Wave w, load i covers tile
+    // rows 16(w + 4i) .. +15; lane l lands in LDS slot l of that 1-KB span,
+    // i.e. row 16(w + 4i) + l/4, physical chunk l%4, so it fetches logical
+    // chunk (l%4) ^ ((row/4)%4) of its row.  Rows past the output width or the
+    // segment point at a valid row (their results are never stored).
+    const int lrow = lane >> 2, lpc = lane & 3;
+    const uint16_t* xsrc[GM_DL];
+    const uint16_t* wsrc[GM_DL];
+    int lchunk[GM_DL];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const int n = n0 + 16 * m + 4 * g;
-            if (n < H) {
-                uint2 o;
-                o.x = pack_bf16x2(acc[m][0], acc[m][1]);
-                o.y = pack_bf16x2(acc[m][2], acc[m][3]);
-                *reinterpret_cast<uint2*>(a.out + (size_t)s * H + n) = o;
+    for (int i = 0; i < GM_DL; ++i) {
+        const int row = 16 * (wave + 4 * i) + lrow;
+        lchunk[i] = lpc ^ ((row >> 2) & 3);
+        const int s = sbase + row;
+        if constexpr (GATE_UP)
+            xsrc[i] = a.x + (size_t)(s < seg1 ? a.sorted_pairs[s] / a.k : 0) * a.H;
+        else
+            xsrc[i] = a.a_rows + (size_t)(s < seg1 ? s : 0) * a.I;
+        if constexpr (WFMT == 0) {
+            const long long wr = gm_wrow<GATE_UP>(a, e, n0, NOUT, row);
+            wsrc[i] = static_cast<const uint16_t*>(a.w) + (size_t)(wr >= 0 ? wr : gm_wrow<GATE_UP>(a, e, 0, NOUT, 0)) * K;
+        } else {
+            wsrc[i] = nullptr;
+        }
+    }
+    typedef __attribute__((address_space(1))) const void* gptr_t;
+    typedef __attribute__((address_space(3))) void* lptr_t;
+    auto direct = [&](const uint16_t* const (&src)[GM_DL], uint8_t* tile, int kk) {
+#pragma unroll
+        for (int i = 0; i < GM_DL; ++i) {
+            __builtin_amdgcn_global_load_lds((gptr_t)(src[i] + kk + 8 * lchunk[i]), (lptr_t)(tile + 16 * (wave + 4 * i) * GM_ROWB), 16,
+                                             0, 0);
+        }
+    };
+
+    // ---- MXFP4 weights: thread t stages tile row t (32 elements = 16 B + one
+    // scale) two stages ahead in registers and decodes it into LDS.  Rows
+    // past the output width read the tile's first row (never stored).
+    const int nstages = K / GM_BK;
+    long long qrow = 0;
+    if constexpr (WFMT == 1) {
+        qrow = gm_wrow<GATE_UP>(a, e, n0, NOUT, tid);
+        if (qrow < 0) qrow = gm_wrow<GATE_UP>(a, e, 0, NOUT, 0);
+    }
+    u32x4 qw[2];
+    uint8_t qsc[2];  // kept as bytes: widening happens at the decode, not at the load
+    // Every load below is issued unconditionally; stages past the end re-read
+    // the last stage into a free buffer, so each stage issues the same number
+    // of loads and the loop body has no branches.
+    auto fetch_q = [&](int set, int st) {
+        const int kk = min(st, nstages - 1) * GM_BK;
+        qw[set] = *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(a.w) + qrow * (K / 2) + kk / 2);
+        qsc[set] = a.w_scale[qrow * (K / 32) + kk / 32];
+    };
+    auto store_q = [&](int set, int buf) {
+        const float sc = e8m0_to_f32(qsc[set]);
+        *reinterpret_cast<u32x4*>(sh.w[buf] + gm_swz(tid, 0)) = fp4x8_to_bf16x8(qw[set].x, sc);
+        *reinterpret_cast<u32x4*>(sh.w[buf] + gm_swz(tid, 1)) = fp4x8_to_bf16x8(qw[set].y, sc);
+        *reinterpret_cast<u32x4*>(sh.w[buf] + gm_swz(tid, 2)) = fp4x8_to_bf16x8(qw[set].z, sc);
+        *reinterpret_cast<u32x4*>(sh.w[buf] + gm_swz(tid, 3)) = fp4x8_to_bf16x8(qw[set].w, sc);
+    };
+    // Vector-memory operations per wave per stage (vmcnt bookkeeping): direct
+    // loads, and the MXFP4 register loads.
+    constexpr int L = (WFMT == 0 ? 2 : 1) * GM_DL;
+    constexpr int QL = WFMT == 1 ? 2 : 0;
+    // Issue the direct loads of stage st into buffer st % NBUF.
+    auto issue = [&](int st) {
+        const int buf = st % GM_NBUF, kk = min(st, nstages - 1) * GM_BK;
+        if constexpr (WFMT == 0) direct(wsrc, sh.w[buf], kk);
+        direct(xsrc, sh.x[buf], kk);
+    };
+
+    f32x16 acc[GM_WB][GM_TB];
+#pragma unroll
+    for (int m = 0; m < GM_WB; ++m)
+#pragma unroll
+        for (int t = 0; t < GM_TB; ++t) acc[m][t] = f32x16{};
+
+    // Operand fragments of one 16-wide K step, read from LDS.
+    struct Frags {
+        bf16x8 w[GM_WB];
+        bf16x8 x[GM_TB];
+    };
+    auto load_frags = [&](int buf, int s, Frags& f) {
+        const int c = 2 * s + kg;
+#pragma unroll
+        for (int t = 0; t < GM_TB; ++t)
+            f.x[t] = as_bf16x8(*reinterpret_cast<const u32x4*>(sh.x[buf] + gm_swz(128 * wt + 32 * t + r32, c)));
+#pragma unroll
+        for (int m = 0; m < GM_WB; ++m)
+            f.w[m] = as_bf16x8(*reinterpret_cast<const u32x4*>(sh.w[buf] + gm_swz(128 * ww + 32 * m + r32, c)));
+    };
+    auto mma = [&](const Frags& f) {
+#pragma unroll
+        for (int m = 0; m < GM_WB; ++m)
+#pragma unroll
+            for (int t = 0; t < GM_TB; ++t) acc[m][t] = mfma32(f.w[m], f.x[t], acc[m][t]);
+    };
+    // One LDS read per two MFMAs, so the reads' latency hides under the MFMAs.
+    auto interleave = [&]() {
+#pragma unroll
+        for (int i = 0; i < GM_WB + GM_TB; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // 2 MFMAs
+        }
+    };
+
+    // Software pipeline.  Each stage is two 16-wide K steps.  The barrier that
+    // publishes stage st+1 sits between the two halves of stage st: the 16
+    // MFMAs of step 0 are issued first and keep the matrix pipe busy while the
+    // wave waits at the barrier; step 1's MFMAs then run while stage st+1's
+    // first fragments are read.  Direct loads run GM_DIST stages ahead, MXFP4
+    // register loads two.  Per stage a wave issues, in order: the register
+    // loads of stage st+3, (barrier), the direct loads of stage st+3.
+    for (int st = 0; st < GM_DIST; ++st) issue(st);
+    if constexpr (WFMT == 1) {
+        fetch_q(0, 0);
+        fetch_q(1, 1);
+        store_q(0, 0);
+        fetch_q(0, 2);
+    }
+    vm_wait<0>();
+    lds_barrier();
+    Frags f0, f1;
+    load_frags(0, 0, f0);
+    // Stage st with st + 1 < nstages.  SET = (st + 1) & 1 is the MXFP4
+    // register set holding stage st+1; a template constant, so that the two
+    // sets stay in fixed registers.
+    auto stage = [&](int st, auto set_c) {
+        constexpr int SET = decltype(set_c)::value;
+        const int buf = st % GM_NBUF, nb = (st + 1) % GM_NBUF;
+        __builtin_amdgcn_sched_barrier(0);
+        load_frags(buf, 1, f1);
+        mma(f0);
+        interleave();
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (WFMT == 1) {
+            store_q(SET, nb);             // stage st+1, fetched two stages ago
+            fetch_q(SET, st + 3);
+        }
+        // Outstanding after this wave's direct loads of stage st+1: register
+        // loads of st+2, direct loads of st+2, register loads of st+3.
+        vm_wait<L + 2 * QL>();
+        lds_barrier();  // stage st+1 visible; buffer of stage st-1 is free
+        issue(st + GM_DIST);
+        __builtin_amdgcn_sched_barrier(0);
+        load_frags(nb, 0, f0);
+        mma(f1);
+        interleave();
+    };
+    int st = 0;
+    for (; st + 2 < nstages; st += 2) {
+        stage(st, std::integral_constant<int, 1>{});
+        stage(st + 1, std::integral_constant<int, 0>{});
+    }
+    if (st + 1 < nstages) stage(st++, std::integral_constant<int, 1>{});
+    __builtin_amdgcn_sched_barrier(0);
+    load_frags(st % GM_NBUF, 1, f1);
+    mma(f0);
+    interleave();
+    mma(f1);
+    mfma_drain();
+    vm_wait<0>();  // the surplus loads past the last stage
+
+    // ---- epilogue: for each (m, t) the lane holds tile weight rows
+    // 128ww + 32m + 8(r/4) + 4(lane/32) + r%4 (r = 0..15) of token
+    // 128wt + 32t + lane%32.
+#pragma unroll
+    for (int t = 0; t < GM_TB; ++t) {
+        const int s = sbase + 128 * wt + 32 * t + r32;
+        if (s >= seg1) continue;
+        if constexpr (GATE_UP) {
+            // blocks m = 0, 1 are gate columns 64ww + 32m .., blocks m + 2 the matching up
+#pragma unroll
+            for (int m = 0; m < GM_WB / 2; ++m) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int col = n0 + 64 * ww + 32 * m + 8 * q + 4 * kg;
+                    if (col < NOUT) {
+                        const f32x16& g = acc[m][t];
+                        const f32x16& u = acc[m + GM_WB / 2][t];
+                        uint2 o;
+                        o.x = pack_bf16x2(silu(g[4 * q + 0]) * u[4 * q + 0], silu(g[4 * q + 1]) * u[4 * q + 1]);
+                        o.y = pack_bf16x2(silu(g[4 * q + 2]) * u[4 * q + 2], silu(g[4 * q + 3]) * u[4 * q + 3]);
+                        *reinterpret_cast<uint2*>(a.out + (size_t)s * NOUT + col) = o;
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int m = 0; m < GM_WB; ++m) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int col = n0 + 128 * ww + 32 * m + 8 * q + 4 * kg;
+                    if (col < NOUT) {
+                        const f32x16& v = acc[m][t];
+                        uint2 o;
+                        o.x = pack_bf16x2(v[4 * q + 0], v[4 * q + 1]);
+                        o.y = pack_bf16x2(v[4 * q + 2], v[4 * q + 3]);
+                        *reinterpret_cast<uint2*>(a.out + (size_t)s * NOUT + col) = o;
+                    }
+                }
             }
         }
     }
 }
 
-static int m_tiles_bound(int P, int E) { return (P + TL_BM - 1) / TL_BM + E; }
+template <int WFMT, bool GATE_UP>
+static hipError_t launch_gemm(const FfnArgs& a, hipStream_t s)
+{
+    const int NOUT = GATE_UP ? a.I : a.H;
+    const int WCOLS = GATE_UP ? GM_BW / 2 : GM_BW;
+    const long long nt = (NOUT + WCOLS - 1) / WCOLS;
+    const long long mt_bound = ((long long)a.T * a.k + GM_BT - 1) / GM_BT + a.E;
+    long long grid = nt * mt_bound;
+    grid = (grid + 7) / 8 * 8;
+    hipLaunchKernelGGL((gemm_kernel<WFMT, GATE_UP>), dim3((unsigned)grid), dim3(GM_THREADS), 0, s, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_gate_up_tiled(const FfnArgs& a, hipStream_t s)
 {
-    dim3 grid((a.I + TL_BW / 2 - 1) / (TL_BW / 2), m_tiles_bound(a.T * a.k, a.E));
-    if (a.wfmt == 0)
-        hipLaunchKernelGGL(gate_up_tiled_kernel<0>, grid, dim3(TL_THREADS), 0, s, a);
-    else
-        hipLaunchKernelGGL(gate_up_tiled_kernel<1>, grid, dim3(TL_THREADS), 0, s, a);
-    return hipGetLastError();
+    return a.wfmt == 0 ? launch_gemm<0, true>(a, s) : launch_gemm<1, true>(a, s);
 }
 
 hipError_t launch_down_tiled(const FfnArgs& a, hipStream_t s)
 {
-    dim3 grid((a.H + TL_BW - 1) / TL_BW, m_tiles_bound(a.T * a.k, a.E));
-    if (a.wfmt == 0)
-        hipLaunchKernelGGL(down_tiled_kernel<0>, grid, dim3(TL_THREADS), 0, s, a);
-    else
-        hipLaunchKernelGGL(down_tiled_kernel<1>, grid, dim3(TL_THREADS), 0, s, a);
-    return hipGetLastError();
+    return a.wfmt == 0 ? launch_gemm<0, false>(a, s) : launch_gemm<1, false>(a, s);
 }
 
 }  // namespace moe
