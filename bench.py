@@ -18,6 +18,14 @@ Prints ONE JSON line.  Besides the headline fields it carries:
                 decode and prefill, the 120b token sweep): us per layer,
                 tokens/s and their roofline fractions.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary]
+
+Traffic measurement (two rocprofv3 counter runs, then a summary):
+  rocprofv3 --pmc FETCH_SIZE -d DIR_F -o run -- python3 bench.py --no-secondary --no-cpu --copy-probe
+  rocprofv3 --pmc WRITE_SIZE -d DIR_W -o run -- python3 bench.py --no-secondary --no-cpu --copy-probe
+  python3 bench.py --write-traffic DIR_F DIR_W OUT.json
+--copy-probe adds launches of a plain elementwise copy (torch.neg on a 1 GiB
+bf16 tensor: 1 GiB read, 1 GiB written) whose counter readings calibrate
+the kernel's: HBM bytes = counter KiB x 1024 x (known bytes / copy's reading).
 """
 from __future__ import annotations
 
@@ -39,6 +47,7 @@ MALL_BYTES = 256 << 20
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {"gate_up_skinny": "mixture_experts_ffn_05_amd/csrc/ffn_skinny.hip",
                   "gate_up_tiled": "mixture_experts_ffn_05_amd/csrc/ffn_tiled.hip"}
+TRAFFIC_FILES = {"gate_up_skinny": "skinny_gate_up_bf16_20b_decode_traffic.json"}
 
 
 def source_digest(rel: str) -> str:
@@ -49,7 +58,7 @@ def source_digest(rel: str) -> str:
 def measured_traffic(kernel: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if
     it was taken on the current source of the kernel (else None)."""
-    path = os.path.join(PROFILE_DIR, f"{kernel}_traffic.json")
+    path = os.path.join(PROFILE_DIR, TRAFFIC_FILES[kernel])
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -94,27 +103,63 @@ class Timed:
         moe.moe_combine(g.dims, g.y_sorted, g.pair_rank, g.topk_w, g.y)
         rec(5)
 
-    def run(self, steps: int, warmup: int, stage_events: bool = True):
+    def forward(self, i: int):
+        """One whole layer through the single fused entry point."""
+        g = self.g
+        self.moe.moe_forward(g.dims, g.x, g.w_router, self.weights[i % len(self.weights)], g.y, None, None, g.ws,
+                             g.ws_bytes)
+
+    def capture(self):
+        """One HIP graph per weight copy, each holding one moe_forward."""
         torch = self.torch
+        self.forward(0)
+        torch.cuda.synchronize()
+        self.graphs = []
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        for i in range(len(self.weights)):
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(s):
+                with torch.cuda.graph(gr, stream=s):
+                    self.forward(i)
+            self.graphs.append(gr)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+
+    def run(self, steps: int, warmup: int, graph: bool = False):
+        """Seconds per layer step (moe_forward, eager launches or a HIP graph
+        replay of the same launches), inputs resident in HBM."""
+        torch = self.torch
+        if graph:
+            self.capture()
+            go = lambda i: self.graphs[i % len(self.graphs)].replay()  # noqa: E731
+        else:
+            go = self.forward
         for i in range(warmup):
-            self.step(i)
+            go(i)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(steps):
-            self.step(i, self.ev[i % len(self.ev)] if stage_events else None)
+            go(i)
         torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        stages = None
-        if stage_events:
-            n = min(steps, len(self.ev))
-            sums = [0.0] * 5
-            for i in range(n):
-                e = self.ev[i]
-                for j in range(5):
-                    sums[j] += e[j].elapsed_time(e[j + 1])
-            stages = {name: 1000.0 * s / n for name, s in
-                      zip(("route", "permute", "gate_up", "down", "combine"), sums)}
-        return wall / steps, stages
+        return (time.perf_counter() - t0) / steps
+
+    def stages(self, steps: int, warmup: int = 3):
+        """Mean microseconds of each stage entry point, from HIP events
+        recorded on the stream the kernels are launched on (torch's current
+        stream, which the binding passes to the library)."""
+        for i in range(warmup):
+            self.step(i)
+        n = min(steps, len(self.ev))
+        for i in range(n):
+            self.step(i, self.ev[i])
+        self.torch.cuda.synchronize()
+        sums = [0.0] * 5
+        for i in range(n):
+            e = self.ev[i]
+            for j in range(5):
+                sums[j] += e[j].elapsed_time(e[j + 1])
+        return {name: 1000.0 * s / n for name, s in zip(("route", "permute", "gate_up", "down", "combine"), sums)}
 
     def touched_experts(self) -> int:
         off = self.g.offsets.cpu().numpy()
@@ -145,7 +190,7 @@ def n_copies_for(cfg, touched_bytes):
     return max(4, min(16, int(4 * MALL_BYTES // max(touched_bytes, 1)) + 1))
 
 
-def bench_decode(layer, steps, warmup):
+def bench_decode(layer, steps, warmup, graph=False):
     import torch
     probe = Timed(layer, 1)
     probe.step(0)
@@ -154,7 +199,8 @@ def bench_decode(layer, steps, warmup):
     total_b, gu_b = layer_bytes(layer.cfg, touched)
     del probe
     tm = Timed(layer, n_copies_for(layer.cfg, total_b))
-    sec, stages = tm.run(steps, warmup)
+    sec = tm.run(steps, warmup, graph)
+    stages = tm.stages(steps)
     return tm, sec, stages, touched, total_b, gu_b
 
 
@@ -177,14 +223,82 @@ def cpu_baseline(layer, min_seconds=10.0):
                       f"{el:.1f} s"}
 
 
-def secondary(steps):
+COPY_PROBE_BYTES = 1 << 30
+COPY_KERNEL_KEY = "neg"
+
+
+def copy_probe(reps: int = 5):
+    """Launches of a plain copy kernel of known size, for counter calibration."""
+    import torch
+    src = torch.ones(COPY_PROBE_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+
+
+def _counter_means(run_dir: str, counter: str):
+    """Mean per-dispatch value of one counter for each kernel name in a
+    rocprofv3 --pmc csv output directory."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {run_dir}")
+    per = {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] != counter:
+                continue
+            key = (r["Kernel_Name"], r["Dispatch_Id"])
+            per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    out = {}
+    for (name, _), v in per.items():
+        out.setdefault(name, []).append(v)
+    return {k: sum(v) / len(v) for k, v in out.items()}
+
+
+DOMINANT_KERNEL = "skinny_kernel<0, true>"  # gate/up + SwiGLU, bf16 weights, skinny regime
+
+
+def write_traffic(fetch_dir: str, write_dir: str, out_path: str, kernel: str = "gate_up_skinny"):
+    """HBM bytes per launch of the dominant kernel from FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch), each scaled by the factor that maps the
+    copy kernel's reading onto its known bytes."""
+    res = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        means = _counter_means(d, counter)
+        copy = [v for k, v in means.items() if COPY_KERNEL_KEY in k]
+        kern = [v for k, v in means.items() if DOMINANT_KERNEL in k]
+        if not copy or not kern:
+            raise SystemExit(f"{counter}: kernels not found in {d}: {sorted(means)}")
+        factor = COPY_PROBE_BYTES / (copy[0] * 1024.0)
+        res[counter] = {"kernel_kib_per_dispatch": kern[0], "copy_kib_per_dispatch": copy[0],
+                        "copy_known_bytes": COPY_PROBE_BYTES, "scale": factor,
+                        "bytes_per_launch": kern[0] * 1024.0 * factor}
+    rec = {"kernel": "moe::" + DOMINANT_KERNEL, "workload": "20b decode, 16 tokens, bf16",
+           "source": KERNEL_SOURCES[kernel], "source_sha256_16": source_digest(KERNEL_SOURCES[kernel]),
+           "commands": ["rocprofv3 --pmc FETCH_SIZE --output-format csv -d FETCH_DIR -o run -- python3 bench.py "
+                        "--steps 20 --warmup 3 --no-secondary --no-cpu --copy-probe",
+                        "rocprofv3 --pmc WRITE_SIZE --output-format csv -d WRITE_DIR -o run -- python3 bench.py "
+                        "--steps 20 --warmup 3 --no-secondary --no-cpu --copy-probe",
+                        "python3 bench.py --write-traffic FETCH_DIR WRITE_DIR OUT.json"],
+           "fetch": res["FETCH_SIZE"], "write": res["WRITE_SIZE"],
+           "hbm_bytes_per_launch": res["FETCH_SIZE"]["bytes_per_launch"] + res["WRITE_SIZE"]["bytes_per_launch"]}
+    with open(out_path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec, indent=1))
+
+
+def secondary(steps, graph=False):
     import synth
     out = {}
     # prefill regimes: MFMA-bound
     for name in ("20b_prefill_zipf", "20b_mxfp4_prefill"):
         layer = synth.make_layer(name)
         tm = Timed(layer, 1)
-        sec, stages = tm.run(max(3, steps // 10), 2)
+        sec = tm.run(max(3, steps // 10), 2)
+        stages = tm.stages(max(3, steps // 10), 1)
         fl, fl_gu = layer_flops(layer.cfg)
         peak = BF16_PEAK_TFLOPS  # the kernels issue bf16 MFMA (MXFP4 decoded to bf16 in LDS)
         out[name] = {"tokens_per_s": round(layer.cfg.T / sec, 1), "us_per_layer": round(sec * 1e6, 1),
@@ -195,7 +309,7 @@ def secondary(steps):
         del tm, layer
     # decode regimes: HBM-bound
     layer = synth.make_layer("20b_mxfp4_decode")
-    tm, sec, stages, touched, total_b, gu_b = bench_decode(layer, steps, 10)
+    tm, sec, stages, touched, total_b, gu_b = bench_decode(layer, steps, 10, graph)
     out["20b_mxfp4_decode"] = {"tokens_per_s": round(layer.cfg.T / sec, 1), "us_per_layer": round(sec * 1e6, 1),
                                "touched_experts": touched, "hbm_frac": round(total_b / sec / 1e9 / HBM_PEAK_GBS, 4),
                                "stages_us": {k: round(v, 1) for k, v in stages.items()}}
@@ -206,7 +320,7 @@ def secondary(steps):
     for T in synth.SWEEP_120B:
         cfg = base.with_T(T)
         layer = synth.Layer(cfg, synth.make_x(cfg), synth.make_router(cfg), w120)
-        tm, sec, stages, touched, total_b, gu_b = bench_decode(layer, steps, 10)
+        tm, sec, stages, touched, total_b, gu_b = bench_decode(layer, steps, 10, graph)
         sweep[str(T)] = {"us_per_layer": round(sec * 1e6, 1), "touched_experts": touched,
                          "hbm_frac": round(total_b / sec / 1e9 / HBM_PEAK_GBS, 4),
                          "gate_up_us": round(stages["gate_up"], 1)}
@@ -222,7 +336,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true", help="also launch a copy kernel of known size")
+    ap.add_argument("--graph", action="store_true", help="replay each layer step as a captured HIP graph")
+    ap.add_argument("--write-traffic", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT_JSON"))
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(*args.write_traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
@@ -237,7 +357,7 @@ def main():
 
     layer = synth.make_layer("20b_decode")
     c = layer.cfg
-    tm, sec, stages, touched, total_b, gu_b = bench_decode(layer, args.steps, args.warmup)
+    tm, sec, stages, touched, total_b, gu_b = bench_decode(layer, args.steps, args.warmup, args.graph)
     gu_us = stages["gate_up"]
     achieved = gu_b / (gu_us * 1e-6) / 1e9
     rec = {
@@ -256,11 +376,12 @@ def main():
         "config": {"workload": "gpt-oss-20b-shaped MoE layer, decode: hidden 2880, 32 experts, top-4, expert width "
                                "2880, 16 tokens, bf16 weights",
                    "tokens": c.T, "hidden": c.H, "experts": c.E, "top_k": c.k, "expert_width": c.I,
-                   "touched_experts": touched, "weight_copies_rotated": len(tm.weights), "parallelism": "none (1 GPU)"},
+                   "touched_experts": touched, "weight_copies_rotated": len(tm.weights), "parallelism": "none (1 GPU)",
+                   "launch": "hip_graph" if args.graph else "eager"},
         "hbm_frac_layer": round(total_b / sec / 1e9 / HBM_PEAK_GBS, 4),
         "layer_gbs": round(total_b / sec / 1e9, 1),
         "stages_us": {k: round(v, 2) for k, v in stages.items()},
-        "roofline": {"kernel": "gate_up_skinny_kernel<0> (gate/up + SwiGLU)", "bound": "hbm",
+        "roofline": {"kernel": "moe::" + DOMINANT_KERNEL + " (gate/up + SwiGLU)", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic("gate_up_skinny"),
@@ -269,9 +390,12 @@ def main():
     if not args.no_secondary:
         del tm
         torch.cuda.empty_cache()
-        rec["secondary"] = secondary(args.steps)
+        rec["secondary"] = secondary(args.steps, args.graph)
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(layer)
+    if args.copy_probe:
+        del tm
+        copy_probe()
     print(json.dumps(rec))
 
 
