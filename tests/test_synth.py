@@ -2,6 +2,7 @@
 import numpy as np
 
 import synth
+from tests.oracle_pins import _golden_rows
 
 
 def test_bf16_round_to_nearest_even():
@@ -30,9 +31,20 @@ def test_mxfp4_quantizer_rounding_and_saturation():
 
 
 def test_presets_match_page_shapes():
+    """The synthetic layers carry the shapes the pages print (fixture
+    tests/golden/gpt_oss_layer_shapes.txt, each value cited there)."""
+    g = {k: int(v) for k, v in _golden_rows("gpt_oss_layer_shapes.txt")}
+    # the page figures agree with each other
+    assert g["experts_20b"] * g["layers_20b"] == g["expert_subnets_20b"]
+    assert g["topk"] * g["layers_20b"] == g["subnets_firing_20b"]
+    assert g["expert_width"] % 256 == g["width_mod_256"] and g["expert_width"] % 128 == g["width_mod_128"]
     c = synth.CONFIGS
-    assert (c["20b_decode"].H, c["20b_decode"].E, c["20b_decode"].k, c["20b_decode"].I) == (2880, 32, 4, 2880)
-    assert c["120b_sweep"].E == 128 and c["20b_mxfp4_prefill"].T == 32768 and c["20b_prefill_zipf"].T == 8192
+    for name in ("20b_decode", "20b_prefill_zipf", "20b_mxfp4_decode", "20b_mxfp4_prefill"):
+        assert (c[name].H, c[name].E, c[name].k, c[name].I) == (g["hidden"], g["experts_20b"], g["topk"],
+                                                                g["expert_width"]), name
+    assert (c["120b_sweep"].H, c["120b_sweep"].E, c["120b_sweep"].k) == (g["hidden"], g["experts_120b"], g["topk"])
+    assert c["20b_mxfp4_prefill"].T == 32768 and c["20b_prefill_zipf"].T == 8192 and c["20b_decode"].T == 16
+    assert c["20b_mxfp4_decode"].wfmt == 1 and c["20b_mxfp4_prefill"].wfmt == 1 and c["20b_decode"].wfmt == 0
     assert (c["tiny"].T, c["tiny"].H, c["tiny"].E, c["tiny"].k, c["tiny"].I) == (64, 256, 8, 2, 512)
 
 
