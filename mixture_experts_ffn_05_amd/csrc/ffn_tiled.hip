@@ -62,14 +62,6 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c)
 // Byte offset of 16-B chunk c (0..3) of row r in a [rows][32] bf16 LDS tile.
 __device__ __forceinline__ int gm_swz(int r, int c) { return r * GM_ROWB + ((c ^ ((r >> 2) & 3)) << 4); }
 
-// Wait until at most n vector-memory operations of this wave are outstanding.
-template <int n>
-__device__ __forceinline__ void vm_wait()
-{
-    static_assert(n >= 0 && n < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
 // Workgroup barrier after this wave's LDS writes have completed.  It carries
 // no memory fence: the direct-to-LDS loads still in flight belong to later
 // stages and are waited for explicitly (vm_wait), and a fence here would make

@@ -80,6 +80,16 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t s)
     return s == 0 ? __uint_as_float(0x00400000u) : __uint_as_float(s << 23);
 }
 
+// Wait until at most n vector-memory operations of this wave are outstanding
+// (s_waitcnt: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at their
+// no-wait maxima).
+template <int n>
+__device__ __forceinline__ void vm_wait()
+{
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
 // --------------------------------------------------------------- wave utils
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (WAVE - 1); }
