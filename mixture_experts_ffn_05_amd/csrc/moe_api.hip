@@ -126,19 +126,18 @@ moe::FfnArgs ffn_args(const moe_dims& d)
 int do_route(const moe_dims& d, const void* x, const void* wr, int32_t* idx, float* w, void* ws, hipStream_t s)
 {
     const Layout L = layout_for(d);
-    double* logits = region<double>(ws, L.logits);
-    int rc = hip_status(moe::launch_router_logits_f64(d.T, d.H, d.E, static_cast<const uint16_t*>(x),
-                                                      static_cast<const uint16_t*>(wr), logits, s));
-    if (rc) return rc;
-    return hip_status(moe::launch_router_select(d.T, d.E, d.k, logits, idx, w, s));
+    return hip_status(moe::launch_router_topk(d.T, d.H, d.E, d.k, static_cast<const uint16_t*>(x),
+                                              static_cast<const uint16_t*>(wr), region<double>(ws, L.logits), idx, w,
+                                              s));
 }
 
-// Route + permute.  When one workgroup can permute all pairs, selection and
-// permutation run as one kernel after the logits kernel.
+// Route + permute.  When one workgroup can permute all pairs (and the router
+// does not already fuse the selection), selection and permutation run as one
+// kernel after the logits kernel.
 int do_route_permute(const moe_dims& d, const void* x, const void* wr, int32_t* idx, float* w, int32_t* off,
                      int32_t* sp, int32_t* pr, void* ws, hipStream_t s)
 {
-    if (!moe::permute_fits_one_block(d.T * d.k)) {
+    if (!moe::permute_fits_one_block(d.T * d.k) || moe::router_fuses_select(d.T, d.E)) {
         int rc = do_route(d, x, wr, idx, w, ws, s);
         if (rc) return rc;
         const Layout L = layout_for(d);

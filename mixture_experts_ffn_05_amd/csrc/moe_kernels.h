@@ -17,6 +17,11 @@ hipError_t launch_router_logits_f64(int T, int H, int E, const uint16_t* x, cons
 // Top-k by logit (ties -> lower index) + softmax over the k, one wave per token.
 hipError_t launch_router_select(int T, int E, int k, const double* logits, int32_t* topk_idx, float* topk_w,
                                 hipStream_t s);
+// Logits + top-k + softmax: one fused matrix-core kernel when
+// router_fuses_select(T, E) (logits then unused), else the two kernels above.
+bool router_fuses_select(int T, int E);
+hipError_t launch_router_topk(int T, int H, int E, int k, const uint16_t* x, const uint16_t* wr, double* logits,
+                              int32_t* topk_idx, float* topk_w, hipStream_t s);
 
 
 // ------------------------------------------------------------------ permute

@@ -88,6 +88,30 @@ def test_exact_ties_go_to_lower_index():
         assert tied == sorted(tied)
 
 
+@pytest.mark.parametrize("shape", [(1037, 96, 5, 2), (1024, 64, 48, 4), (2050, 160, 200, 8), (4096, 2880, 32, 4)],
+                         ids=lambda s: "T{}_H{}_E{}_k{}".format(*s))
+def test_route_many_tokens(shape):
+    """The matrix-core logits path (from 1024 tokens on): token and expert
+    counts off its 16-token / 64-expert tiles, plus exact ties from duplicated
+    router rows, against the oracle's route of every token."""
+    T, H, E, k = shape
+    layer = _layer(T, H, E, k, 32)
+    wr = layer.w_router.copy()
+    wr[E - 1] = wr[0]  # experts 0 and E-1 always tie
+    if E > 3:
+        wr[2] = wr[1]
+    layer = synth.Layer(layer.cfg, layer.x, wr, layer.weights)
+    print(f"[edge] route T={T} H={H} E={E} k={k}", flush=True)
+    _, idx_ref, w_ref = oracle.get().route(layer.x, wr, k)
+    g = GpuLayer(layer)
+    g.route()
+    torch.cuda.synchronize()
+    idx = g.topk_idx.cpu().numpy()
+    mism = np.nonzero((idx != idx_ref).any(1))[0]
+    assert mism.size == 0, f"{mism.size} tokens routed differently, first {mism[:5]}"
+    assert np.max(np.abs(g.topk_w.cpu().numpy() - w_ref)) <= 1e-5
+
+
 def test_empty_batch_is_noop():
     layer = _layer(4, 64, 4, 2, 64)
     g = GpuLayer(layer)
