@@ -9,10 +9,12 @@
 // LDS.  The gate/up kernel holds gate and up rows of the same output columns
 // in one tile and applies silu(gate)*up in registers before writing h.
 //
-// Tile: 256 weight rows x 256 tokens, 4 waves in 2 x 2; a wave owns 128
-// weight rows x 128 tokens = 4 x 4 blocks of 32x32 in 256 accumulator
-// registers, so per 16-wide K step it reads 8 operand fragments from LDS for
-// 16 MFMAs (the next step's fragments are read while the current MFMAs run).
+// Tile: 256 weight rows x 256 tokens, 8 waves (two per SIMD, so one wave's
+// MFMAs run while the other waits on memory or a barrier) in 2 x 4; a wave
+// owns 128 weight rows x 64 tokens = 4 x 2 blocks of 32x32 in 128
+// accumulator registers, so per 16-wide K step it reads 6 operand fragments
+// from LDS for 8 MFMAs (the next step's fragments are read while the current
+// MFMAs run).
 // For gate/up the tile's weight rows are ordered [g0 g1 u0 u1 | g2 g3 u2 u3]
 // (32-row blocks of gate and up rows of the same 128 output columns), so each
 // wave holds matching gate and up blocks.
@@ -42,17 +44,18 @@ namespace moe {
 
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
-constexpr int GM_THREADS = 256;
+constexpr int GM_THREADS = 512;
+constexpr int GM_WAVES = GM_THREADS / WAVE;  // 8: 2 weight halves x 4 token quarters
 constexpr int GM_BT = 256;    // tokens per tile (MFMA N side)
 constexpr int GM_BW = 256;    // weight rows per tile (MFMA M side)
 constexpr int GM_BK = 32;     // K per stage
 constexpr int GM_NBUF = 4;    // LDS stages
 constexpr int GM_DIST = 3;    // bf16 loads run this many stages ahead
 constexpr int GM_WB = 4;      // weight blocks per wave (128 rows)
-constexpr int GM_TB = 4;      // token blocks per wave (128 tokens)
+constexpr int GM_TB = 2;      // token blocks per wave (64 tokens)
 constexpr int GM_BAND = 4;    // M-tiles per band
 constexpr int GM_ROWB = GM_BK * 2;                                   // bytes per LDS row (64)
-constexpr int GM_DL = GM_BW * GM_ROWB / 1024 / (GM_THREADS / WAVE);  // direct loads per wave per operand (4)
+constexpr int GM_DL = GM_BW * GM_ROWB / 1024 / GM_WAVES;  // direct loads per wave per operand (2)
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c)
 {
@@ -144,7 +147,7 @@ __device__ __forceinline__ long long gm_wrow(const FfnArgs& a, int e, int n0, in
 }
 
 template <int WFMT, bool GATE_UP>
-__global__ __launch_bounds__(GM_THREADS, 1) void gemm_kernel(FfnArgs a)
+__global__ __launch_bounds__(GM_THREADS, GM_WAVES / 4) void gemm_kernel(FfnArgs a)
 {
     __shared__ __attribute__((aligned(16))) GmShared sh;
     const int NOUT = GATE_UP ? a.I : a.H;  // output columns
@@ -168,10 +171,10 @@ __global__ __launch_bounds__(GM_THREADS, 1) void gemm_kernel(FfnArgs a)
 
     const int tid = threadIdx.x, lane = lane_id(), wave = tid / WAVE;
     const int r32 = lane & 31, kg = lane >> 5;
-    const int wt = wave & 1, ww = wave >> 1;  // token half, weight half of this wave
+    const int wt = wave % 4, ww = wave / 4;  // token quarter, weight half of this wave
 
     // ---- direct-to-LDS staging of bf16 tiles.  Wave w, load i covers tile
-    // rows 16(w + 4i) .. +15; lane l lands in LDS slot l of that 1-KB span,
+    // rows 16(w + 8i) .. +15; lane l lands in LDS slot l of that 1-KB span,
     // i.e. row 16(w + 4i) + l/4, physical chunk l%4, so it fetches logical
     // chunk (l%4) ^ ((row/4)%4) of its row.  Rows past the output width or the
     // segment point at a valid row (their results are never stored).
@@ -181,7 +184,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void gemm_kernel(FfnArgs a)
     int lchunk[GM_DL];
 #pragma unroll
     for (int i = 0; i < GM_DL; ++i) {
-        const int row = 16 * (wave + 4 * i) + lrow;
+        const int row = 16 * (wave + GM_WAVES * i) + lrow;
         lchunk[i] = lpc ^ ((row >> 2) & 3);
         const int s = sbase + row;
         if constexpr (GATE_UP)
@@ -200,36 +203,36 @@ __global__ __launch_bounds__(GM_THREADS, 1) void gemm_kernel(FfnArgs a)
     auto direct = [&](const uint16_t* const (&src)[GM_DL], uint8_t* tile, int kk) {
 #pragma unroll
         for (int i = 0; i < GM_DL; ++i) {
-            __builtin_amdgcn_global_load_lds((gptr_t)(src[i] + kk + 8 * lchunk[i]), (lptr_t)(tile + 16 * (wave + 4 * i) * GM_ROWB), 16,
+            __builtin_amdgcn_global_load_lds((gptr_t)(src[i] + kk + 8 * lchunk[i]), (lptr_t)(tile + 16 * (wave + GM_WAVES * i) * GM_ROWB), 16,
                                              0, 0);
         }
     };
 
-    // ---- MXFP4 weights: thread t stages tile row t (32 elements = 16 B + one
-    // scale) two stages ahead in registers and decodes it into LDS.  Rows
-    // past the output width read the tile's first row (never stored).
+    // ---- MXFP4 weights: thread t stages half qh = t%2 of tile row t/2 (16
+    // elements = 8 B, and the row's scale) two stages ahead in registers and
+    // decodes it into LDS chunks 2qh, 2qh+1 of the row.  Rows past the output
+    // width read the tile's first row (never stored).
     const int nstages = K / GM_BK;
     long long qrow = 0;
     if constexpr (WFMT == 1) {
-        qrow = gm_wrow<GATE_UP>(a, e, n0, NOUT, tid);
+        qrow = gm_wrow<GATE_UP>(a, e, n0, NOUT, tid >> 1);
         if (qrow < 0) qrow = gm_wrow<GATE_UP>(a, e, 0, NOUT, 0);
     }
-    u32x4 qw[2];
+    const int qh = tid & 1;
+    uint2 qw[2];
     uint8_t qsc[2];  // kept as bytes: widening happens at the decode, not at the load
     // Every load below is issued unconditionally; stages past the end re-read
     // the last stage into a free buffer, so each stage issues the same number
     // of loads and the loop body has no branches.
     auto fetch_q = [&](int set, int st) {
         const int kk = min(st, nstages - 1) * GM_BK;
-        qw[set] = *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(a.w) + qrow * (K / 2) + kk / 2);
+        qw[set] = *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(a.w) + qrow * (K / 2) + kk / 2 + 8 * qh);
         qsc[set] = a.w_scale[qrow * (K / 32) + kk / 32];
     };
     auto store_q = [&](int set, int buf) {
         const float sc = e8m0_to_f32(qsc[set]);
-        *reinterpret_cast<u32x4*>(sh.w[buf] + gm_swz(tid, 0)) = fp4x8_to_bf16x8(qw[set].x, sc);
-        *reinterpret_cast<u32x4*>(sh.w[buf] + gm_swz(tid, 1)) = fp4x8_to_bf16x8(qw[set].y, sc);
-        *reinterpret_cast<u32x4*>(sh.w[buf] + gm_swz(tid, 2)) = fp4x8_to_bf16x8(qw[set].z, sc);
-        *reinterpret_cast<u32x4*>(sh.w[buf] + gm_swz(tid, 3)) = fp4x8_to_bf16x8(qw[set].w, sc);
+        *reinterpret_cast<u32x4*>(sh.w[buf] + gm_swz(tid >> 1, 2 * qh)) = fp4x8_to_bf16x8(qw[set].x, sc);
+        *reinterpret_cast<u32x4*>(sh.w[buf] + gm_swz(tid >> 1, 2 * qh + 1)) = fp4x8_to_bf16x8(qw[set].y, sc);
     };
     // Vector-memory operations per wave per stage (vmcnt bookkeeping): direct
     // loads, and the MXFP4 register loads.
@@ -257,7 +260,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void gemm_kernel(FfnArgs a)
         const int c = 2 * s + kg;
 #pragma unroll
         for (int t = 0; t < GM_TB; ++t)
-            f.x[t] = as_bf16x8(*reinterpret_cast<const u32x4*>(sh.x[buf] + gm_swz(128 * wt + 32 * t + r32, c)));
+            f.x[t] = as_bf16x8(*reinterpret_cast<const u32x4*>(sh.x[buf] + gm_swz(32 * GM_TB * wt + 32 * t + r32, c)));
 #pragma unroll
         for (int m = 0; m < GM_WB; ++m)
             f.w[m] = as_bf16x8(*reinterpret_cast<const u32x4*>(sh.w[buf] + gm_swz(128 * ww + 32 * m + r32, c)));
@@ -268,13 +271,15 @@ __global__ __launch_bounds__(GM_THREADS, 1) void gemm_kernel(FfnArgs a)
 #pragma unroll
             for (int t = 0; t < GM_TB; ++t) acc[m][t] = mfma32(f.w[m], f.x[t], acc[m][t]);
     };
-    // One LDS read per two MFMAs, so the reads' latency hides under the MFMAs.
+    // LDS reads spread evenly among the MFMAs, so their latency hides under them.
     auto interleave = [&]() {
 #pragma unroll
         for (int i = 0; i < GM_WB + GM_TB; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // 2 MFMAs
+            __builtin_amdgcn_sched_group_barrier(0x008, GM_WB * GM_TB / (GM_WB + GM_TB), 0);
         }
+        if constexpr (GM_WB * GM_TB % (GM_WB + GM_TB) != 0)
+            __builtin_amdgcn_sched_group_barrier(0x008, GM_WB * GM_TB % (GM_WB + GM_TB), 0);
     };
 
     // Software pipeline.  Each stage is two 16-wide K steps.  The barrier that
@@ -336,10 +341,10 @@ __global__ __launch_bounds__(GM_THREADS, 1) void gemm_kernel(FfnArgs a)
 
     // ---- epilogue: for each (m, t) the lane holds tile weight rows
     // 128ww + 32m + 8(r/4) + 4(lane/32) + r%4 (r = 0..15) of token
-    // 128wt + 32t + lane%32.
+    // 64wt + 32t + lane%32.
 #pragma unroll
     for (int t = 0; t < GM_TB; ++t) {
-        const int s = sbase + 128 * wt + 32 * t + r32;
+        const int s = sbase + 32 * GM_TB * wt + 32 * t + r32;
         if (s >= seg1) continue;
         if constexpr (GATE_UP) {
             // blocks m = 0, 1 are gate columns 64ww + 32m .., blocks m + 2 the matching up
