@@ -339,6 +339,9 @@ def main():
     ap.add_argument("--copy-probe", action="store_true", help="also launch a copy kernel of known size")
     ap.add_argument("--graph", action="store_true", help="replay each layer step as a captured HIP graph")
     ap.add_argument("--write-traffic", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT_JSON"))
+    ap.add_argument("--only", metavar="WORKLOAD",
+                    help="time just this synthetic workload (e.g. 20b_prefill_zipf) for --steps layer steps and "
+                         "print its line; for profiling one regime")
     args = ap.parse_args()
     if args.write_traffic:
         write_traffic(*args.write_traffic)
@@ -354,6 +357,17 @@ def main():
     import synth
     moe.library()
     torch.cuda.set_device(0)
+
+    if args.only:
+        layer = synth.make_layer(args.only)
+        tm = Timed(layer, 1)
+        sec = tm.run(args.steps, args.warmup)
+        fl, _ = layer_flops(layer.cfg)
+        print(json.dumps({"workload": args.only, "tokens": layer.cfg.T, "steps": args.steps,
+                          "us_per_layer": round(sec * 1e6, 1), "tokens_per_s": round(layer.cfg.T / sec, 1),
+                          "tflops": round(fl / sec / 1e12, 2),
+                          "mfma_bf16_frac": round(fl / sec / 1e12 / BF16_PEAK_TFLOPS, 4)}))
+        return
 
     layer = synth.make_layer("20b_decode")
     c = layer.cfg
