@@ -71,14 +71,58 @@ __device__ void scan_counts_wave0(int* counts, int E, int32_t* offsets)
     if (lane == 0) offsets[E] = run;
 }
 
+// Permutation of P <= 64 pairs by one wave, lane p holding pair p: stable
+// ranks among equal experts from ballots, per-expert counts through LDS
+// (counts [E]), then their exclusive scan.  No barrier: LDS accesses of one
+// wave complete in order.
+__device__ void permute_wave(int P, int E, const int32_t* __restrict__ topk_idx, int32_t* __restrict__ offsets,
+                             int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ pair_rank, int* counts)
+{
+    const int lane = lane_id();
+    const int key = lane < P ? topk_idx[lane] : -1;
+    for (int e = lane; e < E; e += WAVE) counts[e] = 0;
+    const bool valid = key >= 0;
+    uint64_t peers = ballot(valid);
+    const int nbits = key_bits(E);
+    for (int b = 0; b < nbits; ++b) {
+        const bool bit = valid && ((key >> b) & 1);
+        const uint64_t m = ballot(bit);
+        peers &= bit ? m : ~m;
+    }
+    const int rank = __popcll(peers & lanemask_lt());
+    if (valid && rank == 0) counts[key] = __popcll(peers);
+    int run = 0;
+    for (int base = 0; base < E; base += WAVE) {
+        const int e = base + lane;
+        const int c = e < E ? counts[e] : 0;
+        const int ex = wave_excl_scan(c) + run;
+        if (e < E) {
+            counts[e] = ex;
+            offsets[e] = ex;
+        }
+        run = __shfl(ex + c, WAVE - 1, WAVE);
+    }
+    if (lane == 0) offsets[E] = run;
+    if (valid) {
+        const int s = counts[key] + rank;
+        sorted_pairs[s] = lane;
+        pair_rank[lane] = s;
+    }
+}
+
 // Whole permutation of P <= SMALL_P pairs by one workgroup of PB_THREADS:
-// histogram, exclusive scan, then the stable scatter in passes of 1024 pairs.
+// histogram, exclusive scan, then the stable scatter in passes of 1024 pairs
+// (at most 64 pairs: one wave, see permute_wave).
 __device__ void permute_block(int P, int E, const int32_t* __restrict__ topk_idx, int32_t* __restrict__ offsets,
                               int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ pair_rank)
 {
     __shared__ int wave_counts[PB_WAVES * MAX_E];
     __shared__ int chunk_total[MAX_E];
     __shared__ int cursor[MAX_E];
+    if (P <= WAVE) {  // uniform
+        if (threadIdx.x < WAVE) permute_wave(P, E, topk_idx, offsets, sorted_pairs, pair_rank, cursor);
+        return;
+    }
     const int nbits = key_bits(E);
     for (int e = threadIdx.x; e < E; e += blockDim.x) cursor[e] = 0;
     __syncthreads();
