@@ -16,9 +16,9 @@
 //
 // Work item = (a-th touched expert, 32 weight rows): gate/up takes 16 gate
 // rows and the 16 matching up rows, down takes 32 rows of W_down.  The rows
-// are streamed in chunks of 1 KB per row (512 bf16 or 2048 fp4 elements):
-// each wave-wide load reads 1 KB of consecutive bytes of a row, so every
-// access is a long contiguous run.  The grid is persistent: workgroup b takes items b, b+G,
+// are streamed in chunks of 1 KB (bf16) or 512 B (MXFP4) per row; each
+// wave-wide load reads 1 KB of consecutive parts, so every access is a long
+// contiguous run.  The grid is persistent: workgroup b takes items b, b+G,
 // b+2G, ... (consecutive items are neighbouring rows of one expert) and walks
 // the (item, token pass, chunk) sequence as one pipeline -- the next chunk,
 // possibly of the next item, is fetched into registers while the current one
@@ -32,9 +32,12 @@ namespace moe {
 constexpr int SK_ROWS = 32;             // weight rows per item
 constexpr int SK_NG = 1;                // 16-token groups held per pass
 
-// Per weight format: workgroup size and bytes of one row per chunk.  Chunks
-// are 1 KB per row: 512 bf16 elements over 4 waves, or 2048 MXFP4 elements
-// over 8 waves (two workgroups resident per CU either way).
+// Per weight format: workgroup size and bytes of one row per chunk.  The
+// kernel is bound by HBM latency (each workgroup keeps one chunk in flight),
+// so the sizes trade chunk bytes against resident workgroups: bf16 streams
+// 1 KB per row (512 elements over 4 waves, three workgroups per CU); MXFP4
+// streams 512 B per row (1024 elements over 4 waves), which keeps the
+// per-wave registers low enough for four workgroups per CU.
 template <int WFMT>
 struct SkFmt;
 template <>
@@ -46,10 +49,10 @@ struct SkFmt<0> {  // bf16
 };
 template <>
 struct SkFmt<1> {  // MXFP4
-    static constexpr int THREADS = 512;
-    static constexpr int ROW_BYTES = 1024;
+    static constexpr int THREADS = 256;
+    static constexpr int ROW_BYTES = 512;
     static constexpr int KC = ROW_BYTES * 2;
-    static constexpr int MIN_WAVES = 4;       // per SIMD: 2 resident workgroups per CU
+    static constexpr int MIN_WAVES = 4;       // per SIMD: 4 resident workgroups per CU
 };
 template <int WFMT>
 struct SkGeom {
