@@ -60,6 +60,10 @@ def _bind(lib):
     lib.orc_forward_tokens.restype = _I
     lib.orc_forward_tokens.argtypes = [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P,
                                         _I]
+    lib.orc_mxfp4_quantize.restype = _I
+    lib.orc_mxfp4_quantize.argtypes = [_I64, _I64, _P, _P, _P]
+    lib.orc_mxfp4_fakequant.restype = _I
+    lib.orc_mxfp4_fakequant.argtypes = [_I64, _I64, _P, _P]
     lib.orc_max_threads.restype = _I
     lib.orc_max_threads.argtypes = []
     return lib
@@ -159,6 +163,24 @@ class Oracle:
                                                 self._ptr(o), self._ptr(h), threads),
                     "forward_tokens")
         return (y, idx, w, o, h) if want_pairs else (y, idx, w)
+
+    # ------------------------------------------------------------ quantize
+    def mxfp4_quantize(self, w):
+        """bf16 bits [rows][cols] -> (packed u8 [rows][cols/2], scales u8 [rows][cols/32])."""
+        w = np.ascontiguousarray(w, np.uint16)
+        rows, cols = w.shape
+        q = np.empty((rows, cols // 2), np.uint8)
+        s = np.empty((rows, cols // 32), np.uint8)
+        self._check(self.lib.orc_mxfp4_quantize(rows, cols, self._ptr(w), self._ptr(q), self._ptr(s)), "quantize")
+        return q, s
+
+    def mxfp4_fakequant(self, w):
+        """bf16 bits [rows][cols] -> bf16 bits of decode(quantize(w))."""
+        w = np.ascontiguousarray(w, np.uint16)
+        rows, cols = w.shape
+        out = np.empty((rows, cols), np.uint16)
+        self._check(self.lib.orc_mxfp4_fakequant(rows, cols, self._ptr(w), self._ptr(out)), "fakequant")
+        return out
 
     def max_threads(self) -> int:
         return self.lib.orc_max_threads()

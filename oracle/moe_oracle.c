@@ -406,6 +406,116 @@ int orc_forward_tokens(int T, int H, int E, int k, int I, int wfmt,
     return err;
 }
 
+/* ---------------------------------------------------------- quantize */
+
+/* MXFP4 quantizer: the step that produces the experts' MXFP4 weights from
+ * bf16 ones (the QAT run trains through fake-quantised expert weights and
+ * then exports them quantised: "Persona Kappa: training a 20B LLM on desktop
+ * GPUs", section "Quantization-Aware Training (QAT)").  The pages do not
+ * print the rounding rule; this is the OCP Microscaling v1.0 one:
+ *   per block of 32 consecutive elements along a row, with amax = max |v|,
+ *   X = floor(log2 amax) - 2 (2 is the exponent of the largest E2M1
+ *   magnitude, 6 = 1.5 * 2^2) and the E8M0 byte S = clamp(X + 127, 0, 254);
+ *   an all-zero block stores S = 0 and zero codes;
+ *   each element v / 2^(S-127) goes to the nearest E2M1 magnitude (values
+ *   beyond 6 to 6), an exact midpoint to the even code; the sign bit is set
+ *   only on a nonzero code of a negative element. */
+
+/* Nearest of the eight E2M1 magnitudes to mag >= 0; on an exact tie the
+ * even code.  The magnitudes and mag are exact in double, so are the
+ * distances. */
+static unsigned e2m1_nearest(double mag)
+{
+    unsigned best = 0;
+    double bestd = INFINITY;
+    for (unsigned c = 0; c < 8; ++c) {
+        double d = fabs(orc_e2m1_value(c) - mag);
+#if ORC_PLANT == 20
+        int take = d < bestd || (d == bestd && (c % 2 == 1)); /* planted: ties to the odd code */
+#else
+        int take = d < bestd || (d == bestd && (c % 2 == 0));
+#endif
+        if (take) {
+            best = c;
+            bestd = d;
+        }
+    }
+    return best;
+}
+
+/* Quantise one block of 32 bf16 values: 32 codes (low nibble = element 0 of
+ * a pair) and the scale byte. */
+static void quantize_block(const uint16_t* v, uint8_t codes[32], uint8_t* scale)
+{
+    double amax = 0.0;
+    for (int i = 0; i < 32; ++i) amax = fmax(amax, fabs(orc_bf16_value(v[i])));
+    unsigned S = 0;
+    if (amax > 0.0) {
+        int e;
+        frexp(amax, &e); /* amax = m * 2^e, m in [0.5, 1): floor(log2 amax) = e - 1 */
+#if ORC_PLANT == 21
+        int X = (e - 1) - 1; /* planted: one octave too high */
+#else
+        int X = (e - 1) - 2;
+#endif
+        int s = X + 127;
+        S = s < 0 ? 0u : (s > 254 ? 254u : (unsigned)s);
+    }
+    double unit = ldexp(1.0, (int)S - 127);
+    for (int i = 0; i < 32; ++i) {
+        double x = orc_bf16_value(v[i]);
+        unsigned c = amax > 0.0 ? e2m1_nearest(fabs(x) / unit) : 0u;
+#if ORC_PLANT == 22
+        if (x < 0.0 || signbit(x)) c |= 8u; /* planted: negative zero kept */
+#else
+        if (x < 0.0 && c != 0u) c |= 8u;
+#endif
+        codes[i] = (uint8_t)c;
+    }
+    *scale = (uint8_t)S;
+}
+
+/* w bf16 [rows][cols] -> packed u8 [rows][cols/2] (element 2b in the low
+ * nibble of byte b) and scales u8 [rows][cols/32].  cols % 32 == 0. */
+int orc_mxfp4_quantize(int64_t rows, int64_t cols, const uint16_t* w, uint8_t* packed, uint8_t* scales)
+{
+    if (rows < 0 || cols < 0 || cols % 32 != 0 || (rows * cols > 0 && (!w || !packed || !scales))) return ORC_ERR_ARG;
+    const int64_t nb = cols / 32;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t b = 0; b < nb; ++b) {
+            uint8_t codes[32];
+            quantize_block(w + r * cols + 32 * b, codes, scales + r * nb + b);
+            uint8_t* out = packed + r * (cols / 2) + 16 * b;
+            for (int i = 0; i < 16; ++i) out[i] = (uint8_t)(codes[2 * i] | (codes[2 * i + 1] << 4));
+        }
+    return ORC_OK;
+}
+
+/* Fake quantisation: w -> decode(quantize(w)) as bf16 [rows][cols].  Every
+ * decoded value (at most two significant bits, exponent within bf16's range
+ * since S <= 252 for finite bf16 input) is exactly a bf16 value, so the
+ * conversion below does not round; it fails if it would. */
+int orc_mxfp4_fakequant(int64_t rows, int64_t cols, const uint16_t* w, uint16_t* out)
+{
+    if (rows < 0 || cols < 0 || cols % 32 != 0 || (rows * cols > 0 && (!w || !out))) return ORC_ERR_ARG;
+    const int64_t nb = cols / 32;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t b = 0; b < nb; ++b) {
+            uint8_t codes[32], S, bytes[16];
+            quantize_block(w + r * cols + 32 * b, codes, &S);
+            for (int i = 0; i < 16; ++i) bytes[i] = (uint8_t)(codes[2 * i] | (codes[2 * i + 1] << 4));
+            for (int i = 0; i < 32; ++i) {
+                double v = orc_mxfp4_value(bytes, &S, i);
+                float f = (float)v;
+                uint32_t u;
+                memcpy(&u, &f, sizeof u);
+                if ((double)f != v || (u & 0xFFFFu) != 0u) return ORC_ERR_ARG;
+                out[r * cols + 32 * b + i] = (uint16_t)(u >> 16);
+            }
+        }
+    return ORC_OK;
+}
+
 /* Threads the OpenMP runtime will use for a parallel region (1 without it). */
 int orc_max_threads(void)
 {

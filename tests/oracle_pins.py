@@ -8,6 +8,10 @@ each fail at least one pin.
 What pins what:
   - decode: printed tables (tests/golden) for bf16 and E2M1, exhaustive
     16 codes x 255 scales, the nibble-order reading, quantize->decode identity;
+  - quantizer: grid values round-trip over scales 0..252, hand-worked ties,
+    saturation, sign-of-zero and clamp cases, byte equality with the input
+    generator's independent numpy quantizer, fake-quant decode/idempotence/
+    error bound, and MXFP4-vs-fake-quant layer equality;
   - route: brute force (an independent k-pass argmax over numpy logits),
     constructed exact ties, all-zero router, sum of weights, k=1, the k=2
     closed form, shift invariance, k=E full softmax;
@@ -169,6 +173,135 @@ def pin_quantize_decode_identity(o):
     q, s = synth.mxfp4_quantize(w)
     back = o.decode_matrix(1, q[None], s[None], w.shape[0], w.shape[1], 0)
     assert np.array_equal(back, w)
+
+
+# --------------------------------------------------------------------------- quantizer pins
+
+
+def _bf16_exact(vals):
+    """bf16 bits of doubles that are exactly bf16 values (checked)."""
+    f = np.asarray(vals, np.float64).astype(np.float32)
+    assert np.array_equal(f.astype(np.float64), np.asarray(vals, np.float64)), "value not exact in fp32"
+    u = f.view(np.uint32)
+    assert not np.any(u & 0xFFFF), "value not exact in bf16"
+    return (u >> 16).astype(np.uint16)
+
+
+def _codes_of(q):
+    """Unpack [rows][cols/2] bytes into [rows][cols] codes (low nibble first)."""
+    return np.stack([q & 15, q >> 4], axis=-1).reshape(q.shape[0], -1)
+
+
+def pin_quantizer_grid_identity(o):
+    """Grid values E2M1(c) x 2^(S-127), in blocks whose largest magnitude is 4
+    or 6 (so floor(log2 amax) - 2 = S - 127), quantise back to the same codes
+    and scale bytes; -0 becomes code 0.  Scales span 0..252 (bf16 subnormals
+    at the bottom, near bf16's maximum at the top); decoded with the printed
+    E2M1 table."""
+    rng = np.random.default_rng(11)
+    table = golden_e2m1()
+    S = np.concatenate([np.arange(0, 253, 4), [1, 2, 3, 127, 250, 251, 252]]).astype(np.int64)
+    nb = S.size
+    codes = rng.integers(0, 16, size=(nb, 32))
+    codes[:, 5] = rng.choice([6, 7, 14, 15], size=nb)  # amax is 4 or 6 times the scale
+    vals = np.array([[table[int(c)] for c in row] for row in codes]) * np.ldexp(1.0, S - 127)[:, None]
+    w = _bf16_exact(vals.reshape(1, -1))
+    q, s = o.mxfp4_quantize(w)
+    assert np.array_equal(s[0], S.astype(np.uint8)), (s[0], S)
+    want = np.where(codes == 8, 0, codes).reshape(1, -1)
+    assert np.array_equal(_codes_of(q), want)
+
+
+def pin_quantizer_closed_forms(o):
+    """Hand-worked blocks: every E2M1 midpoint goes to the even code, values
+    past 6 saturate, the sign is dropped on code 0, all-zero blocks store scale
+    byte 0, and the shared exponent follows floor(log2 amax) - 2 with the
+    clamp at S = 0 below."""
+    blocks, want_codes, want_S = [], [], []
+
+    def block(vals, codes, S):
+        v = np.zeros(32)
+        c = np.zeros(32, np.int64)
+        v[:len(vals)] = vals
+        c[:len(codes)] = codes
+        blocks.append(v)
+        want_codes.append(c)
+        want_S.append(S)
+
+    # amax 4 -> X = 0: midpoints 0.25 .. 5 and their neighbours
+    block([4.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -0.25, -5.0, 0.3125, 0.6875, 2.625, -3.375, 5.5],
+          [6, 0, 2, 2, 4, 4, 6, 6, 0, 14, 1, 1, 5, 13, 7], 127)
+    # amax 7.5 -> floor(log2) = 2, X = 0: saturation at 6
+    block([7.5, -7.0, 6.5, 0.5], [7, 15, 7, 1], 127)
+    # amax 5.125 * 2^-8 (about 0.02): floor(log2) = -6, X = -8, S = 119; the
+    # elements 5.125, 2.5625, -1.28125 (times 2^-8) sit just past midpoints
+    block([5.125 * 2.0 ** -8, 2.5625 * 2.0 ** -8, -1.28125 * 2.0 ** -8], [7, 5, 11], 119)
+    # all zero, and all negative zero
+    block([], [], 0)
+    block([-0.0] * 32, [0] * 32, 0)
+    # amax 2^-126 (smallest normal): X = -128 clamps to S = 0, element 2^-126 * 2^127 = 2
+    block([2.0 ** -126, 2.0 ** -127], [4, 2], 0)
+    # amax 2^-130 (bf16 subnormal): S = 0, element 2^-130 * 2^127 = 1/8 -> code 0
+    block([2.0 ** -130], [0], 0)
+    w = _bf16_exact(np.array(blocks).reshape(1, -1))
+    q, s = o.mxfp4_quantize(w)
+    assert list(s[0]) == want_S, (list(s[0]), want_S)
+    assert np.array_equal(_codes_of(q)[0], np.concatenate(want_codes)), _codes_of(q)[0].reshape(-1, 32)[:3, :16]
+
+
+def pin_quantizer_vs_generator(o):
+    """On N(0, 0.02) weights and on values spread over 40 octaves, the oracle's
+    quantiser agrees byte for byte with the input generator's numpy one (an
+    independent implementation of the same rule: threshold search instead of
+    a nearest-value scan)."""
+    rng = np.random.default_rng(12)
+    a = rng.standard_normal((8, 256)) * 0.02
+    b = rng.standard_normal((8, 256)) * np.ldexp(1.0, rng.integers(-20, 20, size=(8, 256)))
+    for m in (a, b):
+        w = synth.bf16_from_f32(m.astype(np.float32))
+        q, s = o.mxfp4_quantize(w)
+        q2, s2 = synth.mxfp4_quantize(synth.f32_from_bf16(w).astype(np.float64))
+        assert np.array_equal(s, s2) and np.array_equal(q, q2)
+
+
+def pin_fakequant(o):
+    """decode(quantize(w)) in bf16: equals the printed-table decode of the
+    quantised bytes, is idempotent, and stays within one grid step: the error
+    is at most 2^(S-127) (half the widest gap, 4..6) below the saturation
+    point and at most 2^(S-126) past it."""
+    rng = np.random.default_rng(13)
+    table = golden_e2m1()
+    w = synth.bf16_from_f32((rng.standard_normal((6, 128)) * 0.02).astype(np.float32))
+    fq = o.mxfp4_fakequant(w)
+    q, s = o.mxfp4_quantize(w)
+    codes = _codes_of(q)
+    dec = np.vectorize(lambda c: table[int(c)])(codes) * np.ldexp(1.0, s.astype(np.int64) - 127).repeat(32, axis=1)
+    assert np.array_equal(fq, _bf16_exact(dec))
+    assert np.array_equal(o.mxfp4_fakequant(fq), fq)
+    err = np.abs(synth.f32_from_bf16(fq).astype(np.float64) - synth.f32_from_bf16(w).astype(np.float64))
+    unit = np.ldexp(1.0, s.astype(np.int64) - 127).repeat(32, axis=1)
+    assert np.all(err <= 2 * unit)
+
+
+def pin_quantized_forward_equals_fakequant_forward(o):
+    """The layer with MXFP4 weights quantize(W) and the layer with bf16 weights
+    decode(quantize(W)) compute the same reals, so the oracle's outputs agree
+    exactly (the quantiser and the MXFP4 decode path agree)."""
+    T, H, E, k, I = 6, 64, 4, 2, 96
+    rng = np.random.default_rng(14)
+    x = _bf16(rng.standard_normal((T, H)))
+    wr = _bf16(rng.standard_normal((E, H)) * 0.1)
+    gu = _bf16(rng.standard_normal((E * 2 * I, H)) * 0.05)
+    dn = _bf16(rng.standard_normal((E * H, I)) * 0.05)
+    qgu, sgu = o.mxfp4_quantize(gu)
+    qdn, sdn = o.mxfp4_quantize(dn)
+    wq = synth.Weights(1, qgu.reshape(E, 2 * I, H // 2), qdn.reshape(E, H, I // 2), sgu.reshape(E, 2 * I, H // 32),
+                       sdn.reshape(E, H, I // 32))
+    wf = synth.Weights(0, o.mxfp4_fakequant(gu).reshape(E, 2 * I, H), o.mxfp4_fakequant(dn).reshape(E, H, I))
+    tok = np.arange(T, dtype=np.int32)
+    yq = o.forward_tokens(x, wr, wq, k, I, tok)[0]
+    yf = o.forward_tokens(x, wr, wf, k, I, tok)[0]
+    assert np.array_equal(yq, yf)
 
 
 # --------------------------------------------------------------------------- route pins
