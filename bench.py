@@ -16,7 +16,9 @@ Prints ONE JSON line.  Besides the headline fields it carries:
   cpu_baseline  the CPU oracle timed on this host on the whole 16-token layer;
   secondary     the other workloads (prefill bf16 with Zipf routing, MXFP4
                 decode and prefill, the 120b token sweep): us per layer,
-                tokens/s and their roofline fractions.
+                tokens/s and their roofline fractions; and the MXFP4
+                quantiser / fake quantiser on the 20b gate/up tensor (GB/s
+                against the HBM peak).
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary]
 
 Traffic measurement (two rocprofv3 counter runs, then a summary):
@@ -290,6 +292,44 @@ def write_traffic(fetch_dir: str, write_dir: str, out_path: str, kernel: str = "
     print(json.dumps(rec, indent=1))
 
 
+def bench_quantize(steps: int):
+    """MXFP4 quantiser and fake quantiser on the 20b gate/up tensor
+    ([32*5760][2880] bf16 ~N(0, 0.02), drawn on the device from a seeded
+    generator; 1.06 GB, beyond the Infinity Cache).  Algorithmic bytes per
+    element: 2 read + 1/2 + 1/32 written (quantise), 2 + 2 (fake quantise)."""
+    import torch
+
+    import mixture_experts_ffn_05_amd as moe
+    rows, cols = 32 * 5760, 2880
+    n = rows * cols
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    w = (torch.randn((rows, cols), generator=g, device="cuda") * 0.02).to(torch.bfloat16).view(torch.int16)
+    packed = torch.empty((rows, cols // 2), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device="cuda")
+    fq = torch.empty_like(w)
+    calls = {"quantize": (lambda: moe.moe_mxfp4_quantize(rows, cols, w, packed, scales), n * (2 + 0.5 + 1 / 32)),
+             "fakequant": (lambda: moe.moe_mxfp4_fakequant(rows, cols, w, fq), n * 4.0)}
+    out = {"tensor": f"[{rows}][{cols}] bf16"}
+    reps = max(10, steps // 10)
+    for name, (fn, nbytes) in calls.items():
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        sec = e0.elapsed_time(e1) * 1e-3 / reps
+        out[name] = {"us": round(sec * 1e6, 1), "gbs": round(nbytes / sec / 1e9, 1),
+                     "hbm_frac": round(nbytes / sec / 1e9 / HBM_PEAK_GBS, 4), "algorithmic_bytes": int(nbytes)}
+    del w, packed, scales, fq
+    torch.cuda.empty_cache()
+    return out
+
+
 def secondary(steps, graph=False):
     import synth
     out = {}
@@ -326,6 +366,7 @@ def secondary(steps, graph=False):
                          "gate_up_us": round(stages["gate_up"], 1)}
         del tm, layer
     out["120b_sweep"] = sweep
+    out["mxfp4_quantize_20b_gate_up"] = bench_quantize(steps)
     return out
 
 
@@ -358,6 +399,9 @@ def main():
     moe.library()
     torch.cuda.set_device(0)
 
+    if args.only == "mxfp4_quantize":
+        print(json.dumps({"workload": args.only, **bench_quantize(args.steps)}))
+        return
     if args.only:
         layer = synth.make_layer(args.only)
         tm = Timed(layer, 1)

@@ -161,6 +161,34 @@ int moe_combine(const moe_dims* dims, const void* y_sorted, const int32_t* pair_
 int moe_forward(const moe_dims* dims, const void* x, const void* w_router, const moe_expert_weights* weights, void* y,
                 int32_t* topk_idx_out, float* topk_w_out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* MXFP4 quantisation of bf16 weights: the step that produces MXFP4 expert
+ * weights from bf16 ones ("Persona Kappa: training a 20B LLM on desktop
+ * GPUs", section "Quantization-Aware Training (QAT)": after training through
+ * fake-quantised expert weights, the weights are exported quantised).  The
+ * pages give no rounding rule; this is OCP Microscaling v1.0's.  Per block of
+ * 32 consecutive elements of a row of w bf16 [rows][cols], with amax the
+ * largest |v| of the block:
+ *   S = clamp(floor(log2 amax) - 2 + 127, 0, 254)  stored in scales
+ *       u8 [rows][cols/32]; an all-zero block stores S = 0;
+ *   each element v / 2^(S-127) rounded to the nearest E2M1 value, an exact
+ *   midpoint to the even code, stored in packed u8 [rows][cols/2] (element
+ *   2b in the low nibble of byte b); a zero code never carries the sign bit.
+ * This is the layout the layer's MXFP4 weights use, so a [E][N][K] bf16
+ * tensor quantises with rows = E*N, cols = K.  Inf/NaN inputs give undefined
+ * codes.  Errors: rows or cols < 0 -> MOE_ERR_INVALID_ARG; cols % 32 != 0 or
+ * rows*cols too large for one launch (2^44 elements) -> MOE_ERR_UNSUPPORTED;
+ * w or packed not 16-byte aligned -> MOE_ERR_MISALIGNED; a null pointer ->
+ * MOE_ERR_INVALID_ARG.  rows*cols = 0 returns MOE_OK and launches nothing.
+ * Outputs must not overlap w.  Asynchronous on `stream` like every call. */
+int moe_mxfp4_quantize(int64_t rows, int32_t cols, const void* w, uint8_t* packed, uint8_t* scales, void* stream);
+
+/* Fake quantisation, the forward of training through quantisation (same
+ * section): out bf16 [rows][cols] = the decoded values of
+ * moe_mxfp4_quantize(w), E2M1(code) * 2^(S-127).  Every such value is exactly
+ * a bf16 value, so out is exact.  Same arguments rules as moe_mxfp4_quantize;
+ * out must be 16-byte aligned and must not overlap w. */
+int moe_mxfp4_fakequant(int64_t rows, int32_t cols, const void* w, void* out, void* stream);
+
 /* Static text for an error code. */
 const char* moe_strerror(int code);
 

@@ -22,7 +22,8 @@ MOE_WFMT_BF16, MOE_WFMT_MXFP4 = 0, 1
 MOE_PATH_AUTO, MOE_PATH_SKINNY, MOE_PATH_TILED = 0, 1, 2
 
 EXPORTED = ("moe_workspace_size", "moe_route", "moe_permute", "moe_gate_up", "moe_down", "moe_grouped_ffn",
-            "moe_combine", "moe_forward", "moe_strerror", "moe_last_error")
+            "moe_combine", "moe_forward", "moe_mxfp4_quantize", "moe_mxfp4_fakequant", "moe_strerror",
+            "moe_last_error")
 
 
 class MoeLibraryMissing(RuntimeError):
@@ -71,6 +72,8 @@ def library(path: str | None = None):
         "moe_grouped_ffn": [D, V, V, V, W, V, V, SZ, V],
         "moe_combine": [D, V, V, V, V, V],
         "moe_forward": [D, V, V, W, V, V, V, V, SZ, V],
+        "moe_mxfp4_quantize": [ctypes.c_int64, ctypes.c_int32, V, V, V, V],
+        "moe_mxfp4_fakequant": [ctypes.c_int64, ctypes.c_int32, V, V, V],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -168,6 +171,16 @@ def moe_forward(d, x, w_router, weights: moe_expert_weights, y, topk_idx_out, to
                                                _stream(stream)))
 
 
+def moe_mxfp4_quantize(rows: int, cols: int, w, packed, scales, stream=None):
+    _check("moe_mxfp4_quantize", library().moe_mxfp4_quantize(rows, cols, _ptr(w), _ptr(packed), _ptr(scales),
+                                                             _stream(stream)))
+
+
+def moe_mxfp4_fakequant(rows: int, cols: int, w, out, stream=None):
+    _check("moe_mxfp4_fakequant", library().moe_mxfp4_fakequant(rows, cols, _ptr(w), _ptr(out), _stream(stream)))
+
+
 __all__ = ["library", "dims", "expert_weights", "strerror", "moe_workspace_size", "moe_route", "moe_permute",
-           "moe_gate_up", "moe_down", "moe_grouped_ffn", "moe_combine", "moe_forward", "moe_dims",
+           "moe_gate_up", "moe_down", "moe_grouped_ffn", "moe_combine", "moe_forward", "moe_mxfp4_quantize",
+           "moe_mxfp4_fakequant", "moe_dims",
            "moe_expert_weights", "MoeError", "MoeLibraryMissing", "EXPORTED", "LIB_PATH"]

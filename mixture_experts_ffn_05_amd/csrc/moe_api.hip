@@ -311,6 +311,42 @@ int moe_forward(const moe_dims* dims, const void* x, const void* w_router, const
                                           static_cast<uint16_t*>(y), s));
 }
 
+namespace {
+
+// Shared validation of the quantiser entry points.
+int check_quant(int64_t rows, int32_t cols, const void* w, int64_t* n_elems)
+{
+    if (rows < 0 || cols < 0) return MOE_ERR_INVALID_ARG;
+    if (cols % 32 != 0) return MOE_ERR_UNSUPPORTED;
+    if (rows != 0 && cols != 0 && rows > moe::mxfp4_quant_max_elems() / cols) return MOE_ERR_UNSUPPORTED;
+    *n_elems = rows * (int64_t)cols;
+    if (*n_elems == 0) return MOE_OK;
+    return check_ptr(w, 16);
+}
+
+}  // namespace
+
+int moe_mxfp4_quantize(int64_t rows, int32_t cols, const void* w, uint8_t* packed, uint8_t* scales, void* stream)
+{
+    int64_t n = 0;
+    int rc = check_quant(rows, cols, w, &n);
+    if (rc || n == 0) return rc;
+    if ((rc = check_ptr(packed, 16))) return rc;
+    if (!scales) return MOE_ERR_INVALID_ARG;
+    return hip_status(moe::launch_mxfp4_quantize(static_cast<const uint16_t*>(w), n, packed, scales,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
+int moe_mxfp4_fakequant(int64_t rows, int32_t cols, const void* w, void* out, void* stream)
+{
+    int64_t n = 0;
+    int rc = check_quant(rows, cols, w, &n);
+    if (rc || n == 0) return rc;
+    if ((rc = check_ptr(out, 16))) return rc;
+    return hip_status(moe::launch_mxfp4_fakequant(static_cast<const uint16_t*>(w), n, static_cast<uint16_t*>(out),
+                                                  static_cast<hipStream_t>(stream)));
+}
+
 const char* moe_strerror(int code)
 {
     switch (code) {

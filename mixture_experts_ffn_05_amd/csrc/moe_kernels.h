@@ -57,4 +57,11 @@ hipError_t launch_down_tiled(const FfnArgs& a, hipStream_t s);
 hipError_t launch_combine(int T, int H, int k, const uint16_t* y_sorted, const int32_t* pair_rank,
                           const float* topk_w, uint16_t* y, hipStream_t s);
 
+// ------------------------------------------------------------------ MXFP4 quantiser
+// w bf16 [n_elems] (n_elems % 32 == 0) -> packed [n_elems/2] + scales
+// [n_elems/32], or its decoded bf16 values.
+int64_t mxfp4_quant_max_elems();
+hipError_t launch_mxfp4_quantize(const uint16_t* w, int64_t n_elems, uint8_t* packed, uint8_t* scales, hipStream_t s);
+hipError_t launch_mxfp4_fakequant(const uint16_t* w, int64_t n_elems, uint16_t* out, hipStream_t s);
+
 }  // namespace moe

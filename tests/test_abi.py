@@ -81,3 +81,21 @@ def test_argument_errors_launch_nothing(lib):
     d0 = moe.dims(0, 64, 4, 2, 64)
     assert _call(lib, "moe_forward", byref(d0), None, None, None, None, None, None, None, 0, None) == moe.MOE_OK
     assert lib.moe_strerror(moe.MOE_ERR_WORKSPACE) == b"workspace too small"
+
+
+def test_quantizer_argument_errors_launch_nothing(lib):
+    A = 0x10000  # fake, 16-byte aligned device address: never dereferenced on these paths
+    q, f = lib.moe_mxfp4_quantize, lib.moe_mxfp4_fakequant
+    assert q(-1, 64, A, A, A, None) == moe.MOE_ERR_INVALID_ARG
+    assert q(4, -32, A, A, A, None) == moe.MOE_ERR_INVALID_ARG
+    assert q(4, 48, A, A, A, None) == moe.MOE_ERR_UNSUPPORTED
+    assert q(1 << 40, 2880, A, A, A, None) == moe.MOE_ERR_UNSUPPORTED
+    assert q(4, 64, None, A, A, None) == moe.MOE_ERR_INVALID_ARG
+    assert q(4, 64, A, A, None, None) == moe.MOE_ERR_INVALID_ARG
+    assert q(4, 64, A + 2, A, A, None) == moe.MOE_ERR_MISALIGNED
+    assert q(4, 64, A, A + 4, A + 1, None) == moe.MOE_ERR_MISALIGNED
+    assert f(4, 64, A, A + 2, None) == moe.MOE_ERR_MISALIGNED
+    assert f(4, 33, A, A, None) == moe.MOE_ERR_UNSUPPORTED
+    # an empty tensor is a no-op that succeeds even with null buffers
+    assert q(0, 64, None, None, None, None) == moe.MOE_OK
+    assert f(7, 0, None, None, None) == moe.MOE_OK
