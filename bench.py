@@ -48,8 +48,17 @@ METRIC = "MoE-layer tokens/s + % HBM peak (decode, 16 tok) and % MFMA peak (pref
 MALL_BYTES = 256 << 20
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {"gate_up_skinny": "mixture_experts_ffn_05_amd/csrc/ffn_skinny.hip",
-                  "gate_up_tiled": "mixture_experts_ffn_05_amd/csrc/ffn_tiled.hip"}
-TRAFFIC_FILES = {"gate_up_skinny": "skinny_gate_up_bf16_20b_decode_traffic.json"}
+                  "gate_up_tiled": "mixture_experts_ffn_05_amd/csrc/ffn_tiled.hip",
+                  "mxfp4_quantize": "mixture_experts_ffn_05_amd/csrc/quant.hip"}
+TRAFFIC_FILES = {"gate_up_skinny": "skinny_gate_up_bf16_20b_decode_traffic.json",
+                 "mxfp4_quantize": "mxfp4_quantize_20b_gate_up_traffic.json"}
+# per counter summary: kernel-name pattern, workload, and the bench arguments of the counter runs
+TRAFFIC_RUNS = {
+    "gate_up_skinny": ("skinny_kernel<0, true>", "20b decode, 16 tokens, bf16",
+                       "--steps 20 --warmup 3 --no-secondary --no-cpu --copy-probe"),
+    "mxfp4_quantize": ("mxfp4_quant_kernel<false>", "MXFP4 quantiser on the 20b gate/up tensor [184320][2880] bf16",
+                       "--only mxfp4_quantize --steps 20 --copy-probe"),
+}
 
 
 def source_digest(rel: str) -> str:
@@ -264,27 +273,28 @@ DOMINANT_KERNEL = "skinny_kernel<0, true>"  # gate/up + SwiGLU, bf16 weights, sk
 
 
 def write_traffic(fetch_dir: str, write_dir: str, out_path: str, kernel: str = "gate_up_skinny"):
-    """HBM bytes per launch of the dominant kernel from FETCH_SIZE and
-    WRITE_SIZE (KiB per dispatch), each scaled by the factor that maps the
-    copy kernel's reading onto its known bytes."""
+    """HBM bytes per launch of a kernel (the dominant one by default) from
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled by the factor
+    that maps the copy kernel's reading onto its known bytes."""
+    pattern, workload, run_args = TRAFFIC_RUNS[kernel]
     res = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         means = _counter_means(d, counter)
         copy = [v for k, v in means.items() if COPY_KERNEL_KEY in k]
-        kern = [v for k, v in means.items() if DOMINANT_KERNEL in k]
+        kern = [v for k, v in means.items() if pattern in k]
         if not copy or not kern:
             raise SystemExit(f"{counter}: kernels not found in {d}: {sorted(means)}")
         factor = COPY_PROBE_BYTES / (copy[0] * 1024.0)
         res[counter] = {"kernel_kib_per_dispatch": kern[0], "copy_kib_per_dispatch": copy[0],
                         "copy_known_bytes": COPY_PROBE_BYTES, "scale": factor,
                         "bytes_per_launch": kern[0] * 1024.0 * factor}
-    rec = {"kernel": "moe::" + DOMINANT_KERNEL, "workload": "20b decode, 16 tokens, bf16",
+    rec = {"kernel": "moe::" + pattern, "workload": workload,
            "source": KERNEL_SOURCES[kernel], "source_sha256_16": source_digest(KERNEL_SOURCES[kernel]),
-           "commands": ["rocprofv3 --pmc FETCH_SIZE --output-format csv -d FETCH_DIR -o run -- python3 bench.py "
-                        "--steps 20 --warmup 3 --no-secondary --no-cpu --copy-probe",
-                        "rocprofv3 --pmc WRITE_SIZE --output-format csv -d WRITE_DIR -o run -- python3 bench.py "
-                        "--steps 20 --warmup 3 --no-secondary --no-cpu --copy-probe",
-                        "python3 bench.py --write-traffic FETCH_DIR WRITE_DIR OUT.json"],
+           "commands": [f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d FETCH_DIR -o run -- python3 bench.py "
+                        f"{run_args}",
+                        f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d WRITE_DIR -o run -- python3 bench.py "
+                        f"{run_args}",
+                        f"python3 bench.py --write-traffic FETCH_DIR WRITE_DIR OUT.json --traffic-kernel {kernel}"],
            "fetch": res["FETCH_SIZE"], "write": res["WRITE_SIZE"],
            "hbm_bytes_per_launch": res["FETCH_SIZE"]["bytes_per_launch"] + res["WRITE_SIZE"]["bytes_per_launch"]}
     with open(out_path, "w") as f:
@@ -380,12 +390,14 @@ def main():
     ap.add_argument("--copy-probe", action="store_true", help="also launch a copy kernel of known size")
     ap.add_argument("--graph", action="store_true", help="replay each layer step as a captured HIP graph")
     ap.add_argument("--write-traffic", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT_JSON"))
+    ap.add_argument("--traffic-kernel", default="gate_up_skinny", choices=sorted(TRAFFIC_RUNS),
+                    help="which kernel --write-traffic summarises")
     ap.add_argument("--only", metavar="WORKLOAD",
                     help="time just this synthetic workload (e.g. 20b_prefill_zipf) for --steps layer steps and "
                          "print its line; for profiling one regime")
     args = ap.parse_args()
     if args.write_traffic:
-        write_traffic(*args.write_traffic)
+        write_traffic(*args.write_traffic, kernel=args.traffic_kernel)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -400,7 +412,11 @@ def main():
     torch.cuda.set_device(0)
 
     if args.only == "mxfp4_quantize":
-        print(json.dumps({"workload": args.only, **bench_quantize(args.steps)}))
+        rec = {"workload": args.only, **bench_quantize(args.steps)}
+        rec["traffic_bytes_per_launch"] = measured_traffic("mxfp4_quantize")
+        if args.copy_probe:
+            copy_probe()
+        print(json.dumps(rec))
         return
     if args.only:
         layer = synth.make_layer(args.only)

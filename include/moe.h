@@ -176,7 +176,8 @@ int moe_forward(const moe_dims* dims, const void* x, const void* w_router, const
  * This is the layout the layer's MXFP4 weights use, so a [E][N][K] bf16
  * tensor quantises with rows = E*N, cols = K.  Inf/NaN inputs give undefined
  * codes.  Errors: rows or cols < 0 -> MOE_ERR_INVALID_ARG; cols % 32 != 0 or
- * rows*cols too large for one launch (2^44 elements) -> MOE_ERR_UNSUPPORTED;
+ * rows*cols too large for one launch (over 2^41 elements) ->
+ * MOE_ERR_UNSUPPORTED;
  * w or packed not 16-byte aligned -> MOE_ERR_MISALIGNED; a null pointer ->
  * MOE_ERR_INVALID_ARG.  rows*cols = 0 returns MOE_OK and launches nothing.
  * Outputs must not overlap w.  Asynchronous on `stream` like every call. */

@@ -29,8 +29,12 @@
 
 namespace moe {
 
-constexpr int Q_THREADS = 256;
-constexpr int Q_UNROLL = 4;  // 16-byte slots per thread, all loads issued first
+// Launch shape (measured on the 20b gate/up tensor): 128-thread workgroups;
+// each thread issues its 16-byte loads for all its slots first, two slots
+// when quantising, one when fake quantising (whose output is 4x larger).
+constexpr int Q_THREADS = 128;
+template <bool FAKE>
+constexpr int q_unroll() { return FAKE ? 1 : 2; }
 
 using bf16x2 = __bf16 __attribute__((ext_vector_type(2)));
 
@@ -99,6 +103,7 @@ __global__ __launch_bounds__(Q_THREADS) void mxfp4_quant_kernel(const uint16_t* 
                                                                uint8_t* __restrict__ scales,
                                                                uint16_t* __restrict__ out)
 {
+    constexpr int Q_UNROLL = q_unroll<FAKE>();
     const int64_t base = (int64_t)blockIdx.x * (Q_THREADS * Q_UNROLL) + threadIdx.x;
     u32x4 v[Q_UNROLL];
 #pragma unroll
@@ -117,7 +122,7 @@ __global__ __launch_bounds__(Q_THREADS) void mxfp4_quant_kernel(const uint16_t* 
         const float sc = scale_float(S);
         const uint32_t codes = quantize8(v[u], sc);
         if constexpr (!FAKE) {
-            packed[slot] = codes;
+            __builtin_nontemporal_store(codes, packed + slot);  // streamed out, not re-read here
             if ((threadIdx.x & 3) == 0) scales[slot >> 2] = (uint8_t)S;
         } else {
             u32x4 d;
@@ -125,7 +130,7 @@ __global__ __launch_bounds__(Q_THREADS) void mxfp4_quant_kernel(const uint16_t* 
             d.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 1));
             d.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 2));
             d.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 3));
-            reinterpret_cast<u32x4*>(out)[slot] = d;
+            __builtin_nontemporal_store(d, reinterpret_cast<u32x4*>(out) + slot);
         }
     }
 }
@@ -134,7 +139,7 @@ static hipError_t launch_quant(bool fake, const uint16_t* w, int64_t n_elems, ui
                                uint16_t* out, hipStream_t s)
 {
     const int64_t n_slots = n_elems / 8;
-    const int64_t per_block = Q_THREADS * Q_UNROLL;
+    const int64_t per_block = Q_THREADS * (fake ? q_unroll<true>() : q_unroll<false>());
     const int64_t grid = (n_slots + per_block - 1) / per_block;
     if (fake)
         hipLaunchKernelGGL(mxfp4_quant_kernel<true>, dim3((unsigned)grid), dim3(Q_THREADS), 0, s, w, n_slots, nullptr,
@@ -145,7 +150,9 @@ static hipError_t launch_quant(bool fake, const uint16_t* w, int64_t n_elems, ui
     return hipGetLastError();
 }
 
-int64_t mxfp4_quant_max_elems() { return (int64_t)0x7FFFFFFF * Q_THREADS * Q_UNROLL * 8; }
+// Largest tensor one launch covers (grid x-dimension below 2^31 at the
+// smallest slots-per-workgroup).
+int64_t mxfp4_quant_max_elems() { return (int64_t)0x7FFFFFFF * Q_THREADS * 8; }
 
 hipError_t launch_mxfp4_quantize(const uint16_t* w, int64_t n_elems, uint8_t* packed, uint8_t* scales, hipStream_t s)
 {
