@@ -18,6 +18,8 @@ properties of the whole tensor.
 """
 from __future__ import annotations
 
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -157,3 +159,53 @@ def test_full_20b_gate_up_tensor():
     torch.cuda.synchronize()
     assert torch.equal(fq2, fq)
     assert torch.equal(packed2, packed) and torch.equal(scales2, scales)
+
+
+@pytest.mark.parametrize("name", ["tiny", "20b_decode"])
+def test_fake_quant_forward(name):
+    """The forward of training through quantisation: bf16 expert weights
+    fake-quantised on the GPU, then the bf16 layer; and the MXFP4 layer on the
+    GPU-quantised bytes.  Both compute the oracle's MXFP4 layer on the
+    oracle-quantised weights (the two forms are the same reals, a pin of the
+    oracle), within the layer tolerance."""
+    from tests.gpu_layer import GpuLayer, bf16_dev_to_f64, rel_err
+    print(f"fake-quant forward {name}", flush=True)
+    layer = synth.make_layer(name)
+    c = layer.cfg
+    gu = layer.weights.gate_up.reshape(c.E * 2 * c.I, c.H)
+    dn = layer.weights.down.reshape(c.E * c.H, c.I)
+    o = oracle.get()
+    qgu, sgu = o.mxfp4_quantize(gu)
+    qdn, sdn = o.mxfp4_quantize(dn)
+    wq = synth.Weights(1, qgu.reshape(c.E, 2 * c.I, c.H // 2), qdn.reshape(c.E, c.H, c.I // 2),
+                       sgu.reshape(c.E, 2 * c.I, c.H // 32), sdn.reshape(c.E, c.H, c.I // 32))
+    tokens = synth.sample_tokens(c.T, 512, c.seed + 1)
+    ref = o.forward_tokens(layer.x, layer.w_router, wq, c.k, c.I, tokens)[0]
+
+    # bf16 layer on fake-quantised weights
+    g = GpuLayer(layer)
+    fgu = torch.empty_like(g.gate_up)
+    fdn = torch.empty_like(g.down)
+    moe.moe_mxfp4_fakequant(gu.shape[0], c.H, g.gate_up, fgu)
+    moe.moe_mxfp4_fakequant(dn.shape[0], c.I, g.down, fdn)
+    g.gate_up, g.down = fgu, fdn
+    g.set_path(moe.MOE_PATH_AUTO)
+    g.forward()
+    torch.cuda.synchronize()
+    err = rel_err(bf16_dev_to_f64(g.y)[tokens], ref)
+    assert err <= 1e-2, f"fake-quant bf16 layer: max err {err:.3g} of max|ref|"
+
+    # MXFP4 layer on GPU-quantised bytes
+    cq = dataclasses.replace(c, wfmt=1)
+    lq = synth.Layer(cq, layer.x, layer.w_router, wq)
+    g4 = GpuLayer(lq)
+    # quantise the bf16 weights on the GPU into the MXFP4 layer's buffers
+    # (gate/up from the original weights; down from its fake-quantised copy,
+    # whose re-quantisation gives the same bytes)
+    moe.moe_mxfp4_quantize(gu.shape[0], c.H, to_dev(gu), g4.gate_up, g4.gate_up_scale)
+    moe.moe_mxfp4_quantize(dn.shape[0], c.I, fdn, g4.down, g4.down_scale)
+    g4.forward()
+    torch.cuda.synchronize()
+    assert np.array_equal(g4.gate_up.cpu().numpy(), wq.gate_up) and np.array_equal(g4.down.cpu().numpy(), wq.down)
+    err4 = rel_err(bf16_dev_to_f64(g4.y)[tokens], ref)
+    assert err4 <= 1e-2, f"MXFP4 layer on GPU-quantised weights: max err {err4:.3g} of max|ref|"
