@@ -180,6 +180,48 @@ __device__ __forceinline__ bool ranks_before(double v, int i, double bv, int bi)
     return v > bv || (v == bv && i < bi);
 }
 
+// Per-wave LDS for wave_topk_softmax_rank.
+struct TopkScratch {
+    double v[WAVE];    // the token's logits, lane e holding expert e
+    double sel_v[8];   // selected logits by slot
+};
+
+// Top-k for E <= 64 by one wave, lane e holding expert e: each lane counts
+// the experts that rank before its own (larger logit, or equal logit and a
+// lower index) over all E logits staged in LDS, so its rank is exact and the
+// k lanes with rank < k own the slots -- no serial arg-max rounds.  Then the
+// softmax over the k selected, summed in slot order exactly as
+// wave_topk_softmax does, so both give the same weights.  Lane j writes slot j.
+__device__ __forceinline__ void wave_topk_softmax_rank(const double* row, int E, int k, int32_t* __restrict__ idx_out,
+                                                       float* __restrict__ w_out, TopkScratch& sc)
+{
+    const int e = lane_id();
+    const double v = e < E ? row[e] : -__builtin_inf();
+    sc.v[e] = v;
+    __builtin_amdgcn_wave_barrier();
+    int rank = 0;
+    for (int j = 0; j < E; ++j) rank += ranks_before(sc.v[j], j, v, e) ? 1 : 0;
+    if (e < E && rank < k) {
+        sc.sel_v[rank] = v;
+        idx_out[rank] = e;
+    }
+    __builtin_amdgcn_wave_barrier();
+    double sv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sv[j] = j < k ? sc.sel_v[j] : 0.0;
+    double z = 0.0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        if (j < k) z += exp(sv[j] - sv[0]);
+    if (e < k) {
+        double mine = sv[0];
+#pragma unroll
+        for (int j = 1; j < 8; ++j)
+            if (e == j) mine = sv[j];
+        w_out[e] = (float)(exp(mine - sv[0]) / z);
+    }
+}
+
 // Top-k of one token's E logits (row: global or LDS) by one wave: k rounds of
 // a wave-wide arg-max (each lane owns experts lane, lane+64, ...), then the
 // softmax over the k selected.  Lane j writes slot j.

@@ -162,8 +162,14 @@ __global__ __launch_bounds__(PB_THREADS) void select_permute_small_kernel(
     float* __restrict__ topk_w, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs,
     int32_t* __restrict__ pair_rank)
 {
-    for (int t = threadIdx.x / WAVE; t < T; t += PB_WAVES)
-        wave_topk_softmax(logits + (size_t)t * E, E, k, topk_idx + (size_t)t * k, topk_w + (size_t)t * k);
+    __shared__ TopkScratch sc[PB_WAVES];
+    for (int t = threadIdx.x / WAVE; t < T; t += PB_WAVES) {
+        if (E <= WAVE)
+            wave_topk_softmax_rank(logits + (size_t)t * E, E, k, topk_idx + (size_t)t * k, topk_w + (size_t)t * k,
+                                   sc[threadIdx.x / WAVE]);
+        else
+            wave_topk_softmax(logits + (size_t)t * E, E, k, topk_idx + (size_t)t * k, topk_w + (size_t)t * k);
+    }
     __syncthreads();  // this workgroup's topk_idx stores are visible to it after the barrier
     permute_block(T * k, E, topk_idx, offsets, sorted_pairs, pair_rank);
 }
