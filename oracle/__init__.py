@@ -60,6 +60,10 @@ def _bind(lib):
     lib.orc_forward_tokens.restype = _I
     lib.orc_forward_tokens.argtypes = [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P,
                                         _I]
+    lib.orc_backward.restype = _I
+    lib.orc_backward.argtypes = [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I]
+    lib.orc_backward_f64.restype = _I
+    lib.orc_backward_f64.argtypes = [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
     lib.orc_mxfp4_quantize.restype = _I
     lib.orc_mxfp4_quantize.argtypes = [_I64, _I64, _P, _P, _P]
     lib.orc_mxfp4_fakequant.restype = _I
@@ -163,6 +167,33 @@ class Oracle:
                                                 self._ptr(o), self._ptr(h), threads),
                     "forward_tokens")
         return (y, idx, w, o, h) if want_pairs else (y, idx, w)
+
+    # ------------------------------------------------------------ backward
+    def backward(self, x, w_router, gate_up, down, dy, k: int, threads: int = 0):
+        """bf16 bits: x, dy [T][H], w_router [E][H], gate_up [E][2I][H], down [E][H][I].
+        Returns (dx [T][H], dw_router [E][H], dgate_up [E][2I][H], ddown [E][H][I]) in float64."""
+        T, H = x.shape
+        E, twoI, _ = gate_up.shape
+        I = twoI // 2
+        out = (np.empty((T, H)), np.empty((E, H)), np.empty((E, 2 * I, H)), np.empty((E, H, I)))
+        args = [np.ascontiguousarray(a, np.uint16) for a in (x, w_router, gate_up, down, dy)]
+        self._check(self.lib.orc_backward(T, H, E, k, I, *[self._ptr(a) for a in args], *[self._ptr(o) for o in out],
+                                          threads), "backward")
+        return out
+
+    def backward_f64(self, x, w_router, gate_up, down, dy, k: int):
+        """Double inputs; returns (dx, dw_router, dgate_up, ddown, loss, topk_idx)."""
+        T, H = x.shape
+        E, twoI, _ = gate_up.shape
+        I = twoI // 2
+        out = (np.empty((T, H)), np.empty((E, H)), np.empty((E, 2 * I, H)), np.empty((E, H, I)))
+        loss = np.zeros(1)
+        idx = np.empty((T, k), np.int32)
+        args = [np.ascontiguousarray(a, np.float64) for a in (x, w_router, gate_up, down, dy)]
+        self._check(self.lib.orc_backward_f64(T, H, E, k, I, *[self._ptr(a) for a in args],
+                                              *[self._ptr(o) for o in out], self._ptr(loss), self._ptr(idx)),
+                    "backward_f64")
+        return (*out, float(loss[0]), idx)
 
     # ------------------------------------------------------------ quantize
     def mxfp4_quantize(self, w):

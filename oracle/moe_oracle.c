@@ -406,6 +406,269 @@ int orc_forward_tokens(int T, int H, int E, int k, int I, int wfmt,
     return err;
 }
 
+/* ---------------------------------------------------------- backward */
+
+/* Gradients of the layer (the training variant: the pages fine-tune every
+ * expert's parameters in bf16 with fp32 reductions, "Persona Kappa: training
+ * a 20B LLM on desktop GPUs", section "Techniques That Made It Fit"), for the
+ * loss L = sum_t dy[t] . y[t], i.e. the backward pass given the upstream
+ * gradient dy.  The selection of the k experts is piecewise constant in the
+ * logits, so gradients flow only through the k selected softmax weights.
+ * Per slot j of token t with expert e (forward as above):
+ *   dw_j   = dy . o_j
+ *   do_j   = w_j dy
+ *   da     = Wd^T do_j                     dWd[e]  += do_j a^T
+ *   dg     = da * u * silu'(g)             silu'(z) = s(z) (1 + z (1 - s(z))),  s = logistic
+ *   du     = da * silu(g)                  dWgu[e] += [dg; du] x^T
+ *   dx    += Wg^T dg + Wu^T du
+ * and per token, through the softmax over the k selected logits:
+ *   dl_j   = w_j (dw_j - sum_i w_i dw_i)
+ *   dx    += sum_j dl_j Wr[e_j]             dWr[e_j] += dl_j x
+ * All in double, from the exact input values. */
+
+static double logistic(double z) { return 1.0 / (1.0 + exp(-z)); }
+
+static double silu_grad(double z)
+{
+    double s = logistic(z);
+#if ORC_PLANT == 30
+    return s; /* planted: the z s (1 - s) term dropped */
+#else
+    return s * (1.0 + z * (1.0 - s));
+#endif
+}
+
+/* Source of one expert's weights as doubles: bf16 bit patterns decoded, or
+ * double arrays used in place. */
+typedef struct {
+    const uint16_t* gate_up_bf16;
+    const uint16_t* down_bf16;
+    const double* gate_up_f64;
+    const double* down_f64;
+} weights_src;
+
+static void expert_weights_f64(const weights_src* src, int H, int I, int e, double* wgu, double* wd)
+{
+    const int64_t ngu = 2 * (int64_t)I * H, nd = (int64_t)H * I;
+    if (src->gate_up_f64) {
+        memcpy(wgu, src->gate_up_f64 + e * ngu, sizeof(double) * (size_t)ngu);
+        memcpy(wd, src->down_f64 + e * nd, sizeof(double) * (size_t)nd);
+    } else {
+        for (int64_t i = 0; i < ngu; ++i) wgu[i] = orc_bf16_value(src->gate_up_bf16[e * ngu + i]);
+        for (int64_t i = 0; i < nd; ++i) wd[i] = orc_bf16_value(src->down_bf16[e * nd + i]);
+    }
+}
+
+/* The backward of T tokens.  x, dy [T][H] and wr [E][H] as doubles; outputs
+ * (all overwritten): dx [T][H], dwr [E][H], dgu [E][2I][H], ddn [E][H][I];
+ * optional: loss (sum dy . y), idx_out [T][k]. */
+static int backward_core(int T, int H, int E, int k, int I, const double* x, const double* wr,
+                         const weights_src* src, const double* dy, double* dx, double* dwr, double* dgu,
+                         double* ddn, double* loss, int32_t* idx_out)
+{
+    const size_t Tk = (size_t)(T > 0 ? T : 1) * (size_t)k;
+    int32_t* idx = (int32_t*)malloc(sizeof(int32_t) * Tk);
+    double* w = (double*)malloc(sizeof(double) * Tk);
+    double* dw = (double*)calloc(Tk, sizeof(double));
+    double* lg = (double*)malloc(sizeof(double) * (size_t)E);
+    int* order = (int*)malloc(sizeof(int) * (size_t)E);
+    double* wgu = (double*)malloc(sizeof(double) * (size_t)2 * I * H);
+    double* wd = (double*)malloc(sizeof(double) * (size_t)H * I);
+    int32_t* list = (int32_t*)malloc(sizeof(int32_t) * Tk);
+    /* per pair of the current expert: a, do, and [dg; du] */
+    double *pa = NULL, *pdo = NULL, *pdgu = NULL;
+    int err = ORC_ERR_NOMEM;
+    if (!idx || !w || !dw || !lg || !order || !wgu || !wd || !list) goto done;
+    memset(dx, 0, sizeof(double) * (size_t)T * H);
+    memset(dwr, 0, sizeof(double) * (size_t)E * H);
+    memset(dgu, 0, sizeof(double) * (size_t)E * 2 * I * H);
+    memset(ddn, 0, sizeof(double) * (size_t)E * H * I);
+    /* routing */
+    for (int t = 0; t < T; ++t) {
+        for (int e = 0; e < E; ++e) {
+            double acc = 0.0;
+            for (int h = 0; h < H; ++h) acc += x[(int64_t)t * H + h] * wr[(int64_t)e * H + h];
+            lg[e] = acc;
+        }
+        select_topk_one(E, k, lg, idx + (size_t)t * k, w + (size_t)t * k, order);
+    }
+    double total = 0.0;
+    for (int e = 0; e < E; ++e) {
+        int n = 0;
+        for (int q = 0; q < T * k; ++q)
+            if (idx[q] == e) list[n++] = q;
+        if (n == 0) continue;
+        expert_weights_f64(src, H, I, e, wgu, wd);
+        free(pa);
+        free(pdo);
+        free(pdgu);
+        pa = (double*)malloc(sizeof(double) * (size_t)n * I);
+        pdo = (double*)malloc(sizeof(double) * (size_t)n * H);
+        pdgu = (double*)malloc(sizeof(double) * (size_t)n * 2 * I);
+        if (!pa || !pdo || !pdgu) goto done;
+        double part = 0.0;
+        /* per pair: forward, dw, do, da, [dg; du], dx (a token occurs at most
+         * once per expert, so the dx rows of one expert's pairs are distinct) */
+#pragma omp parallel for schedule(dynamic, 1) reduction(+ : part)
+        for (int j = 0; j < n; ++j) {
+            const int q = list[j], t = q / k;
+            const double* xr = x + (int64_t)t * H;
+            const double* dyr = dy + (int64_t)t * H;
+            double* g = (double*)malloc(sizeof(double) * (size_t)2 * I); /* g then u */
+            double* da = (double*)malloc(sizeof(double) * (size_t)I);
+            if (!g || !da) {
+                free(g);
+                free(da);
+                continue;
+            }
+            double* a = pa + (int64_t)j * I;
+            double* dor = pdo + (int64_t)j * H;
+            double* dgur = pdgu + (int64_t)j * 2 * I;
+            for (int r = 0; r < 2 * I; ++r) {
+                double acc = 0.0;
+                for (int h = 0; h < H; ++h) acc += xr[h] * wgu[(int64_t)r * H + h];
+                g[r] = acc;
+            }
+            for (int i = 0; i < I; ++i) a[i] = silu(g[i]) * g[I + i];
+            double dwq = 0.0;
+            for (int nn = 0; nn < H; ++nn) {
+                double o = 0.0;
+                for (int i = 0; i < I; ++i) o += a[i] * wd[(int64_t)nn * I + i];
+                dwq += dyr[nn] * o;
+            }
+            dw[q] = dwq;
+            part += w[q] * dwq;
+            for (int nn = 0; nn < H; ++nn) dor[nn] = w[q] * dyr[nn];
+            for (int i = 0; i < I; ++i) {
+                double acc = 0.0;
+                for (int nn = 0; nn < H; ++nn) acc += dor[nn] * wd[(int64_t)nn * I + i];
+                da[i] = acc;
+            }
+            for (int i = 0; i < I; ++i) {
+                dgur[i] = da[i] * g[I + i] * silu_grad(g[i]);
+                dgur[I + i] = da[i] * silu(g[i]);
+            }
+            double* dxr = dx + (int64_t)t * H;
+            for (int h = 0; h < H; ++h) {
+                double acc = 0.0;
+                for (int r = 0; r < 2 * I; ++r) acc += dgur[r] * wgu[(int64_t)r * H + h];
+                dxr[h] += acc;
+            }
+            free(g);
+            free(da);
+        }
+        total += part;
+        /* weight gradients, summed over the expert's pairs in list order */
+        double* dde = ddn + (int64_t)e * H * I;
+#pragma omp parallel for schedule(static)
+        for (int nn = 0; nn < H; ++nn)
+            for (int i = 0; i < I; ++i) {
+                double acc = 0.0;
+                for (int j = 0; j < n; ++j) acc += pdo[(int64_t)j * H + nn] * pa[(int64_t)j * I + i];
+#if ORC_PLANT == 31
+                dde[(int64_t)i * H + nn % I] = acc; /* planted: written transposed (square case) */
+#else
+                dde[(int64_t)nn * I + i] = acc;
+#endif
+            }
+        double* dge = dgu + (int64_t)e * 2 * I * H;
+#pragma omp parallel for schedule(static)
+        for (int r = 0; r < 2 * I; ++r)
+            for (int h = 0; h < H; ++h) {
+                double acc = 0.0;
+                for (int j = 0; j < n; ++j) acc += pdgu[(int64_t)j * 2 * I + r] * x[(int64_t)(list[j] / k) * H + h];
+                dge[(int64_t)r * H + h] = acc;
+            }
+    }
+    /* router, through the softmax over the k selected logits */
+    for (int t = 0; t < T; ++t) {
+        double sbar = 0.0;
+        for (int j = 0; j < k; ++j) sbar += w[(size_t)t * k + j] * dw[(size_t)t * k + j];
+        for (int j = 0; j < k; ++j) {
+            const size_t q = (size_t)t * k + j;
+#if ORC_PLANT == 32
+            const double dl = w[q] * dw[q]; /* planted: the mean term dropped */
+#else
+            const double dl = w[q] * (dw[q] - sbar);
+#endif
+            const int e = idx[q];
+            for (int h = 0; h < H; ++h) {
+                dx[(int64_t)t * H + h] += dl * wr[(int64_t)e * H + h];
+                dwr[(int64_t)e * H + h] += dl * x[(int64_t)t * H + h];
+            }
+        }
+    }
+    if (loss) *loss = total;
+    if (idx_out) memcpy(idx_out, idx, sizeof(int32_t) * (size_t)T * k);
+    err = ORC_OK;
+done:
+    free(idx);
+    free(w);
+    free(dw);
+    free(lg);
+    free(order);
+    free(wgu);
+    free(wd);
+    free(list);
+    free(pa);
+    free(pdo);
+    free(pdgu);
+    return err;
+}
+
+static int backward_args_ok(int T, int H, int E, int k, int I)
+{
+    return T >= 0 && H > 0 && E > 0 && k >= 1 && k <= E && I > 0;
+}
+
+/* bf16 inputs (x, dy [T][H]; w_router [E][H]; gate_up [E][2I][H]; down
+ * [E][H][I]) -> double gradients dx [T][H], dw_router [E][H], dgate_up
+ * [E][2I][H], ddown [E][H][I]. */
+int orc_backward(int T, int H, int E, int k, int I, const uint16_t* x, const uint16_t* w_router,
+                 const uint16_t* gate_up, const uint16_t* down, const uint16_t* dy, double* dx, double* dw_router,
+                 double* dgate_up, double* ddown, int threads)
+{
+    if (!backward_args_ok(T, H, E, k, I) || !x || !w_router || !gate_up || !down || !dy || !dx || !dw_router ||
+        !dgate_up || !ddown)
+        return ORC_ERR_ARG;
+#ifdef _OPENMP
+    if (threads > 0) omp_set_num_threads(threads);
+#else
+    (void)threads;
+#endif
+    const size_t nx = (size_t)(T > 0 ? T : 1) * H;
+    double* xd = (double*)malloc(sizeof(double) * nx);
+    double* dyd = (double*)malloc(sizeof(double) * nx);
+    double* wrd = (double*)malloc(sizeof(double) * (size_t)E * H);
+    int err = ORC_ERR_NOMEM;
+    if (xd && dyd && wrd) {
+        for (size_t i = 0; i < (size_t)T * H; ++i) {
+            xd[i] = orc_bf16_value(x[i]);
+            dyd[i] = orc_bf16_value(dy[i]);
+        }
+        for (size_t i = 0; i < (size_t)E * H; ++i) wrd[i] = orc_bf16_value(w_router[i]);
+        weights_src src = {gate_up, down, NULL, NULL};
+        err = backward_core(T, H, E, k, I, xd, wrd, &src, dyd, dx, dw_router, dgate_up, ddown, NULL, NULL);
+    }
+    free(xd);
+    free(dyd);
+    free(wrd);
+    return err;
+}
+
+/* The same on double inputs (for finite-difference checks), also returning
+ * the loss sum_t dy[t] . y[t] and the routing. */
+int orc_backward_f64(int T, int H, int E, int k, int I, const double* x, const double* w_router,
+                     const double* gate_up, const double* down, const double* dy, double* dx, double* dw_router,
+                     double* dgate_up, double* ddown, double* loss, int32_t* idx_out)
+{
+    if (!backward_args_ok(T, H, E, k, I) || !x || !w_router || !gate_up || !down || !dy || !dx || !dw_router ||
+        !dgate_up || !ddown)
+        return ORC_ERR_ARG;
+    weights_src src = {NULL, NULL, gate_up, down};
+    return backward_core(T, H, E, k, I, x, w_router, &src, dy, dx, dw_router, dgate_up, ddown, loss, idx_out);
+}
+
 /* ---------------------------------------------------------- quantize */
 
 /* MXFP4 quantizer: the step that produces the experts' MXFP4 weights from

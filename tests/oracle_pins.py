@@ -12,6 +12,9 @@ What pins what:
     saturation, sign-of-zero and clamp cases, byte equality with the input
     generator's independent numpy quantizer, fake-quant decode/idempotence/
     error bound, and MXFP4-vs-fake-quant layer equality;
+  - backward: central finite differences of the loss sum(dy * y), torch
+    float64 autograd of an independent implementation of the layer, the zero
+    router gradient at E = 1, exact linearity in dy, bf16-vs-double entry;
   - route: brute force (an independent k-pass argmax over numpy logits),
     constructed exact ties, all-zero router, sum of weights, k=1, the k=2
     closed form, shift invariance, k=E full softmax;
@@ -302,6 +305,101 @@ def pin_quantized_forward_equals_fakequant_forward(o):
     yq = o.forward_tokens(x, wr, wq, k, I, tok)[0]
     yf = o.forward_tokens(x, wr, wf, k, I, tok)[0]
     assert np.array_equal(yq, yf)
+
+
+# --------------------------------------------------------------------------- backward pins
+
+
+def _bwd_inputs(seed, T, H, E, k, I, scale=0.3):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((T, H))
+    wr = rng.standard_normal((E, H)) * scale
+    wgu = rng.standard_normal((E, 2 * I, H)) * scale
+    wd = rng.standard_normal((E, H, I)) * scale
+    dy = rng.standard_normal((T, H))
+    return x, wr, wgu, wd, dy
+
+
+def pin_backward_finite_differences(o):
+    """Central differences of the oracle's own loss sum(dy * y) (double
+    inputs, step 1e-6) match its analytic gradients on sampled entries of x,
+    W_router, W_gate_up (gate and up rows) and W_down, at points where the
+    routing does not change within the step."""
+    T, H, E, k, I = 5, 8, 4, 2, 6
+    x, wr, wgu, wd, dy = _bwd_inputs(21, T, H, E, k, I)
+    dx, dwr, dgu, ddn, _, idx = o.backward_f64(x, wr, wgu, wd, dy, k)
+    grads = {"x": dx, "wr": dwr, "wgu": dgu, "wd": ddn}
+    rng = np.random.default_rng(22)
+    eps = 1e-6
+    for name in ("x", "wr", "wgu", "wd"):
+        for _ in range(10):
+            arrs = {"x": x.copy(), "wr": wr.copy(), "wgu": wgu.copy(), "wd": wd.copy()}
+            pos = tuple(int(rng.integers(n)) for n in arrs[name].shape)
+            lv = []
+            for sgn in (1.0, -1.0):
+                a = {kk: v.copy() for kk, v in arrs.items()}
+                a[name][pos] += sgn * eps
+                r = o.backward_f64(a["x"], a["wr"], a["wgu"], a["wd"], dy, k)
+                assert np.array_equal(r[5], idx), "routing changed within the step"
+                lv.append(r[4])
+            fd = (lv[0] - lv[1]) / (2 * eps)
+            g = grads[name][pos]
+            assert abs(fd - g) <= 1e-6 * max(1.0, abs(g)), (name, pos, fd, g)
+
+
+def _torch_layer_grads(x, wr, wgu, wd, dy, k):
+    """The layer written again with torch float64 ops (top-k by a descending
+    sort of the logits; inputs have no ties) and differentiated by autograd."""
+    import torch
+    t = {n: torch.tensor(v, dtype=torch.float64, requires_grad=True)
+         for n, v in (("x", x), ("wr", wr), ("wgu", wgu), ("wd", wd))}
+    I = wd.shape[2]
+    logits = t["x"] @ t["wr"].T
+    sel = torch.argsort(logits.detach(), dim=1, descending=True)[:, :k]
+    w = torch.softmax(torch.gather(logits, 1, sel), dim=1)
+    y = torch.zeros_like(t["x"])
+    for j in range(k):
+        e = sel[:, j]
+        gu = torch.einsum("th,trh->tr", t["x"], t["wgu"][e])
+        a = torch.nn.functional.silu(gu[:, :I]) * gu[:, I:]
+        o_ = torch.einsum("ti,thi->th", a, t["wd"][e])
+        y = y + w[:, j:j + 1] * o_
+    (y * torch.tensor(dy)).sum().backward()
+    return [t[n].grad.numpy() for n in ("x", "wr", "wgu", "wd")], sel.numpy()
+
+
+def pin_backward_torch_autograd(o):
+    """All four gradients equal torch's autograd of an independent float64
+    implementation of the layer, on a non-square shape (H != I) where most
+    experts have tokens and one may have none."""
+    T, H, E, k, I = 9, 12, 5, 2, 7
+    x, wr, wgu, wd, dy = _bwd_inputs(23, T, H, E, k, I)
+    dx, dwr, dgu, ddn, _, idx = o.backward_f64(x, wr, wgu, wd, dy, k)
+    (tx, twr, tgu, tdn), sel = _torch_layer_grads(x, wr, wgu, wd, dy, k)
+    assert np.array_equal(sel, idx)
+    for got, want in ((dx, tx), (dwr, twr), (dgu, tgu), (ddn, tdn)):
+        assert np.allclose(got, want, rtol=1e-10, atol=1e-12), float(np.max(np.abs(got - want)))
+
+
+def pin_backward_special_cases(o):
+    """E = 1, k = 1: the weight is 1 whatever the logit, so the router
+    gradient is exactly zero; gradients are linear in dy (doubling dy doubles
+    every gradient exactly); the bf16 entry point equals the double one on the
+    same values."""
+    x, wr, wgu, wd, dy = _bwd_inputs(24, 4, 6, 1, 1, 5)
+    r = o.backward_f64(x, wr, wgu, wd, dy, 1)
+    assert np.all(r[1] == 0.0)
+    x, wr, wgu, wd, dy = _bwd_inputs(25, 6, 8, 4, 2, 8)
+    a = o.backward_f64(x, wr, wgu, wd, dy, 2)
+    b = o.backward_f64(x, wr, wgu, wd, 2.0 * dy, 2)
+    for u, v in zip(a[:4], b[:4]):
+        assert np.array_equal(2.0 * u, v)
+    bf = [_bf16(v) for v in (x, wr, wgu, wd, dy)]
+    dec = [synth.f32_from_bf16(v).astype(np.float64) for v in bf]
+    c = o.backward(*bf, 2)
+    d = o.backward_f64(*dec, 2)
+    for u, v in zip(c, d[:4]):
+        assert np.array_equal(u, v)
 
 
 # --------------------------------------------------------------------------- route pins

@@ -5,7 +5,9 @@ Planted mistakes: 1 gate/up rows swapped, 2 ties to the higher expert index,
 3 W_down read transposed, 4 unstable permutation, 5 MXFP4 nibble order
 swapped, 6 silu sign error, 7 routing weights not normalised, 20 quantizer
 ties to the odd code, 21 quantizer shared exponent one octave high, 22
-quantizer keeps negative zero."""
+quantizer keeps negative zero, 30 silu derivative missing a term, 31 W_down
+gradient written transposed, 32 router gradient without the softmax mean
+term."""
 import pytest
 
 import oracle
@@ -13,7 +15,8 @@ from tests import oracle_pins
 
 PLANTS = {1: "gate_up_swapped", 2: "tie_to_higher_index", 3: "down_transposed", 4: "unstable_permute",
           5: "nibble_order_swapped", 6: "silu_sign", 7: "weights_unnormalised", 20: "quant_ties_odd",
-          21: "quant_exponent_high", 22: "quant_negative_zero"}
+          21: "quant_exponent_high", 22: "quant_negative_zero", 30: "bwd_silu_grad", 31: "bwd_down_transposed",
+          32: "bwd_router_mean"}
 
 
 @pytest.mark.parametrize("plant", sorted(PLANTS), ids=lambda p: PLANTS[p])
