@@ -161,6 +161,35 @@ int moe_combine(const moe_dims* dims, const void* y_sorted, const int32_t* pair_
 int moe_forward(const moe_dims* dims, const void* x, const void* w_router, const moe_expert_weights* weights, void* y,
                 int32_t* topk_idx_out, float* topk_w_out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Backward of moe_forward (the training variant: every expert's parameters
+ * are fine-tuned in bf16 with fp32 reductions, "Persona Kappa: training a
+ * 20B LLM on desktop GPUs", section "Techniques That Made It Fit"), for
+ * bf16 weights (dims->wfmt = MOE_WFMT_BF16, else MOE_ERR_UNSUPPORTED).
+ * Given the upstream gradient dy bf16 [T][H] of the layer output y, it
+ * recomputes the forward (routing, permutation, gate/up, down) and writes the
+ * gradients of L = sum_t dy[t] . y[t]:
+ *   dx         bf16 [T][H]      w.r.t. x: through the experts and the router
+ *   dw_router  fp32 [E][H]      w.r.t. w_router
+ *   dgate_up   fp32 [E][2I][H]  w.r.t. weights->gate_up (gate rows, then up)
+ *   ddown      fp32 [E][H][I]   w.r.t. weights->down
+ * Per slot j of token t with expert e: dw_j = dy . o_j, do_j = w_j dy,
+ * da = Wd^T do_j, dg = da * u * silu'(g), du = da * silu(g),
+ * dx += Wg^T dg + Wu^T du, dWd[e] += do_j a^T, dWgu[e] += [dg; du] x^T; per
+ * token through the softmax over the k selected logits,
+ * dl_j = w_j (dw_j - sum_i w_i dw_i), dx += sum_j dl_j Wr[e_j],
+ * dWr[e_j] += dl_j x.  The top-k selection itself is piecewise constant and
+ * passes no gradient.  Products run on bf16 MFMA with fp32 accumulation;
+ * intermediates (w dy, g and u, [dg; du], per-pair dx) are stored in bf16.
+ * An expert that receives no token gets zero weight gradients; T = 0 writes
+ * zeros to the three weight gradients and touches nothing else.
+ * Workspace: moe_backward_workspace_size() bytes (it includes the forward's
+ * workspace).  Alignment as above; the fp32 outputs need 4 bytes.  Outputs
+ * must not overlap inputs or each other. */
+int moe_backward_workspace_size(const moe_dims* dims, size_t* bytes);
+int moe_backward(const moe_dims* dims, const void* x, const void* w_router, const moe_expert_weights* weights,
+                 const void* dy, void* dx, float* dw_router, float* dgate_up, float* ddown, void* workspace,
+                 size_t workspace_bytes, void* stream);
+
 /* MXFP4 quantisation of bf16 weights: the step that produces MXFP4 expert
  * weights from bf16 ones ("Persona Kappa: training a 20B LLM on desktop
  * GPUs", section "Quantization-Aware Training (QAT)": after training through

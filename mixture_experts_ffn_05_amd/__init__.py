@@ -22,7 +22,7 @@ MOE_WFMT_BF16, MOE_WFMT_MXFP4 = 0, 1
 MOE_PATH_AUTO, MOE_PATH_SKINNY, MOE_PATH_TILED = 0, 1, 2
 
 EXPORTED = ("moe_workspace_size", "moe_route", "moe_permute", "moe_gate_up", "moe_down", "moe_grouped_ffn",
-            "moe_combine", "moe_forward", "moe_mxfp4_quantize", "moe_mxfp4_fakequant", "moe_strerror",
+            "moe_combine", "moe_forward", "moe_backward_workspace_size", "moe_backward", "moe_mxfp4_quantize", "moe_mxfp4_fakequant", "moe_strerror",
             "moe_last_error")
 
 
@@ -72,6 +72,8 @@ def library(path: str | None = None):
         "moe_grouped_ffn": [D, V, V, V, W, V, V, SZ, V],
         "moe_combine": [D, V, V, V, V, V],
         "moe_forward": [D, V, V, W, V, V, V, V, SZ, V],
+        "moe_backward_workspace_size": [D, ctypes.POINTER(SZ)],
+        "moe_backward": [D, V, V, W, V, V, V, V, V, V, SZ, V],
         "moe_mxfp4_quantize": [ctypes.c_int64, ctypes.c_int32, V, V, V, V],
         "moe_mxfp4_fakequant": [ctypes.c_int64, ctypes.c_int32, V, V, V],
     }
@@ -171,6 +173,19 @@ def moe_forward(d, x, w_router, weights: moe_expert_weights, y, topk_idx_out, to
                                                _stream(stream)))
 
 
+def moe_backward_workspace_size(d: moe_dims) -> int:
+    n = ctypes.c_size_t(0)
+    _check("moe_backward_workspace_size", library().moe_backward_workspace_size(ctypes.byref(d), ctypes.byref(n)))
+    return n.value
+
+
+def moe_backward(d, x, w_router, weights: moe_expert_weights, dy, dx, dw_router, dgate_up, ddown, ws, ws_bytes,
+                 stream=None):
+    _check("moe_backward", library().moe_backward(ctypes.byref(d), _ptr(x), _ptr(w_router), ctypes.byref(weights),
+                                                 _ptr(dy), _ptr(dx), _ptr(dw_router), _ptr(dgate_up), _ptr(ddown),
+                                                 _ptr(ws), ws_bytes, _stream(stream)))
+
+
 def moe_mxfp4_quantize(rows: int, cols: int, w, packed, scales, stream=None):
     _check("moe_mxfp4_quantize", library().moe_mxfp4_quantize(rows, cols, _ptr(w), _ptr(packed), _ptr(scales),
                                                              _stream(stream)))
@@ -181,6 +196,7 @@ def moe_mxfp4_fakequant(rows: int, cols: int, w, out, stream=None):
 
 
 __all__ = ["library", "dims", "expert_weights", "strerror", "moe_workspace_size", "moe_route", "moe_permute",
-           "moe_gate_up", "moe_down", "moe_grouped_ffn", "moe_combine", "moe_forward", "moe_mxfp4_quantize",
+           "moe_gate_up", "moe_down", "moe_grouped_ffn", "moe_combine", "moe_forward", "moe_backward_workspace_size",
+           "moe_backward", "moe_mxfp4_quantize",
            "moe_mxfp4_fakequant", "moe_dims",
            "moe_expert_weights", "MoeError", "MoeLibraryMissing", "EXPORTED", "LIB_PATH"]

@@ -360,6 +360,13 @@ __global__ __launch_bounds__(GM_THREADS, GM_WAVES / 4) void gemm_kernel(FfnArgs 
                         o.x = pack_bf16x2(silu(g[4 * q + 0]) * u[4 * q + 0], silu(g[4 * q + 1]) * u[4 * q + 1]);
                         o.y = pack_bf16x2(silu(g[4 * q + 2]) * u[4 * q + 2], silu(g[4 * q + 3]) * u[4 * q + 3]);
                         *reinterpret_cast<uint2*>(a.out + (size_t)s * NOUT + col) = o;
+                        if (a.gu_out) {  // pre-activations kept for the backward
+                            uint16_t* gu = a.gu_out + (size_t)s * 2 * NOUT + col;
+                            *reinterpret_cast<uint2*>(gu) = uint2{pack_bf16x2(g[4 * q + 0], g[4 * q + 1]),
+                                                                  pack_bf16x2(g[4 * q + 2], g[4 * q + 3])};
+                            *reinterpret_cast<uint2*>(gu + NOUT) = uint2{pack_bf16x2(u[4 * q + 0], u[4 * q + 1]),
+                                                                         pack_bf16x2(u[4 * q + 2], u[4 * q + 3])};
+                        }
                     }
                 }
             }

@@ -181,9 +181,160 @@ int do_down(const moe_dims& d, const void* h, const int32_t* off, const moe_expe
     return hip_status(use_skinny(d) ? moe::launch_down_skinny(a, s) : moe::launch_down_tiled(a, s));
 }
 
+// Backward workspace: the forward's regions first (the stages reuse them),
+// then the saved activations, the gradients in flight, the transposed
+// weights and the per-expert transposed segments (Ppad rows each).
+struct BwdLayout {
+    size_t gu, dO, dw, da, dgu, dxp, padoff, dlT, wdT, wguT, dOT, hT, dguT, xT, total;
+};
+
+BwdLayout bwd_layout_for(const moe_dims& d)
+{
+    const size_t P = (size_t)d.T * (size_t)d.k, H = (size_t)d.H, I = (size_t)d.I, E = (size_t)d.E;
+    const size_t Ppad = (size_t)moe::backward_pad_rows((int)P, d.E);
+    BwdLayout L;
+    size_t at = align_up(layout_for(d).total);
+    auto take = [&](size_t bytes) {
+        size_t here = at;
+        at = align_up(at + bytes);
+        return here;
+    };
+    L.gu = take(P * 2 * I * 2);
+    L.dO = take(P * H * 2);
+    L.dw = take(P * sizeof(float));
+    L.da = take(P * I * 2);
+    L.dgu = take(P * 2 * I * 2);
+    L.dxp = take(P * H * 2);
+    L.padoff = take((E + 1) * sizeof(int32_t));
+    L.dlT = take(Ppad * 2);
+    L.wdT = take(E * H * I * 2);
+    L.wguT = take(E * 2 * I * H * 2);
+    L.dOT = take(H * Ppad * 2);
+    L.hT = take(I * Ppad * 2);
+    L.dguT = take(2 * I * Ppad * 2);
+    L.xT = take(H * Ppad * 2);
+    L.total = at;
+    return L;
+}
+
 }  // namespace
 
 extern "C" {
+
+int moe_backward_workspace_size(const moe_dims* dims, size_t* bytes)
+{
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    if (!bytes) return MOE_ERR_INVALID_ARG;
+    if (dims->wfmt != MOE_WFMT_BF16) return MOE_ERR_UNSUPPORTED;
+    *bytes = bwd_layout_for(*dims).total;
+    return MOE_OK;
+}
+
+int moe_backward(const moe_dims* dims, const void* x, const void* w_router, const moe_expert_weights* weights,
+                 const void* dy, void* dx, float* dw_router, float* dgate_up, float* ddown, void* workspace,
+                 size_t workspace_bytes, void* stream)
+{
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    const moe_dims& d = *dims;
+    if (d.wfmt != MOE_WFMT_BF16) return MOE_ERR_UNSUPPORTED;
+    if (!dw_router || !dgate_up || !ddown) return MOE_ERR_INVALID_ARG;
+    if (!aligned(dw_router, 4) || !aligned(dgate_up, 4) || !aligned(ddown, 4)) return MOE_ERR_MISALIGNED;
+    if ((rc = check_weights(d, weights)) || (rc = check_ptr(w_router, 16))) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const long long nr = (long long)d.E * d.H, ngu = (long long)d.E * 2 * d.I * d.H, nd = (long long)d.E * d.H * d.I;
+    if (d.T == 0) {  // no tokens: every weight gradient is zero
+        if ((rc = hip_status(moe::launch_zero_f32(dw_router, nr, s)))) return rc;
+        if ((rc = hip_status(moe::launch_zero_f32(dgate_up, ngu, s)))) return rc;
+        return hip_status(moe::launch_zero_f32(ddown, nd, s));
+    }
+    if ((rc = check_ptr(x, 16)) || (rc = check_ptr(dy, 16)) || (rc = check_ptr(dx, 16))) return rc;
+    const BwdLayout B = bwd_layout_for(d);
+    if (workspace_bytes < B.total) return MOE_ERR_WORKSPACE;
+    if ((rc = check_ptr(workspace, 16))) return rc;
+    const Layout L = layout_for(d);
+    void* ws = workspace;
+    const int P = d.T * d.k, H = d.H, I = d.I, E = d.E;
+    int32_t* idx = region<int32_t>(ws, L.topk_idx);
+    float* w = region<float>(ws, L.topk_w);
+    int32_t* off = region<int32_t>(ws, L.offsets);
+    int32_t* sp = region<int32_t>(ws, L.sorted);
+    int32_t* pr = region<int32_t>(ws, L.rank);
+    uint16_t* h = region<uint16_t>(ws, L.h);
+    uint16_t* ys = region<uint16_t>(ws, L.y_sorted);
+    uint16_t* gu = region<uint16_t>(ws, B.gu);
+    uint16_t* dO = region<uint16_t>(ws, B.dO);
+    float* dw = region<float>(ws, B.dw);
+    uint16_t* da = region<uint16_t>(ws, B.da);
+    uint16_t* dgu = region<uint16_t>(ws, B.dgu);
+    uint16_t* dxp = region<uint16_t>(ws, B.dxp);
+    int32_t* padoff = region<int32_t>(ws, B.padoff);
+    uint16_t* dlT = region<uint16_t>(ws, B.dlT);
+    uint16_t* wdT = region<uint16_t>(ws, B.wdT);
+    uint16_t* wguT = region<uint16_t>(ws, B.wguT);
+    uint16_t* dOT = region<uint16_t>(ws, B.dOT);
+    uint16_t* hT = region<uint16_t>(ws, B.hT);
+    uint16_t* dguT = region<uint16_t>(ws, B.dguT);
+    uint16_t* xT = region<uint16_t>(ws, B.xT);
+    const uint16_t* xb = static_cast<const uint16_t*>(x);
+    const uint16_t* wgu = static_cast<const uint16_t*>(weights->gate_up);
+    const uint16_t* wdn = static_cast<const uint16_t*>(weights->down);
+
+    // forward, keeping g and u (tiled schedule: it is the one that stores them)
+    if ((rc = do_route_permute(d, x, w_router, idx, w, off, sp, pr, ws, s))) return rc;
+    moe::FfnArgs a = ffn_args(d);
+    a.x = xb;
+    a.offsets = off;
+    a.sorted_pairs = sp;
+    a.w = wgu;
+    a.out = h;
+    a.gu_out = gu;
+    if ((rc = hip_status(moe::launch_gate_up_tiled(a, s)))) return rc;
+    a = ffn_args(d);
+    a.offsets = off;
+    a.a_rows = h;
+    a.w = wdn;
+    a.out = ys;
+    if ((rc = hip_status(moe::launch_down_tiled(a, s)))) return rc;
+    // combine backward: dO = w dy per sorted row, dw = dy . o
+    if ((rc = hip_status(moe::launch_combine_bwd(P, H, d.k, static_cast<const uint16_t*>(dy), ys, sp, w, dO, dw, s))))
+        return rc;
+    // data gradients on transposed weights, through the down-projection kernel
+    if ((rc = hip_status(moe::launch_transpose_batched(wdn, wdT, E, H, I, s)))) return rc;      // [E][I][H]
+    if ((rc = hip_status(moe::launch_transpose_batched(wgu, wguT, E, 2 * I, H, s)))) return rc;  // [E][H][2I]
+    a = ffn_args(d);
+    a.H = I;  // output width
+    a.I = H;  // contracted width
+    a.offsets = off;
+    a.a_rows = dO;
+    a.w = wdT;
+    a.out = da;
+    if ((rc = hip_status(moe::launch_down_tiled(a, s)))) return rc;
+    if ((rc = hip_status(moe::launch_swiglu_bwd(P, I, da, gu, dgu, s)))) return rc;
+    a = ffn_args(d);
+    a.H = H;
+    a.I = 2 * I;
+    a.offsets = off;
+    a.a_rows = dgu;
+    a.w = wguT;
+    a.out = dxp;
+    if ((rc = hip_status(moe::launch_down_tiled(a, s)))) return rc;
+    // router backward and dx
+    if ((rc = hip_status(moe::launch_pad_offsets(off, E, padoff, dlT, s)))) return rc;
+    if ((rc = hip_status(moe::launch_router_bwd(d.T, H, d.k, static_cast<const uint16_t*>(w_router), idx, w, dw, pr,
+                                                off, padoff, dxp, dlT, static_cast<uint16_t*>(dx), s))))
+        return rc;
+    // weight gradients over each expert's transposed, zero-padded segment
+    if ((rc = hip_status(moe::launch_transpose_segments(dO, H, false, off, padoff, sp, d.k, P, E, dOT, s)))) return rc;
+    if ((rc = hip_status(moe::launch_transpose_segments(h, I, false, off, padoff, sp, d.k, P, E, hT, s)))) return rc;
+    if ((rc = hip_status(moe::launch_transpose_segments(dgu, 2 * I, false, off, padoff, sp, d.k, P, E, dguT, s))))
+        return rc;
+    if ((rc = hip_status(moe::launch_transpose_segments(xb, H, true, off, padoff, sp, d.k, P, E, xT, s)))) return rc;
+    if ((rc = hip_status(moe::launch_wgrad(dOT, hT, padoff, E, H, I, ddown, s)))) return rc;
+    if ((rc = hip_status(moe::launch_wgrad(dguT, xT, padoff, E, 2 * I, H, dgate_up, s)))) return rc;
+    return hip_status(moe::launch_wgrad(dlT, xT, padoff, E, 1, H, dw_router, s));
+}
 
 int moe_workspace_size(const moe_dims* dims, size_t* bytes)
 {

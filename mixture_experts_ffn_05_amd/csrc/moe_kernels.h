@@ -47,6 +47,7 @@ struct FfnArgs {
     const uint8_t* w_scale;     // MXFP4 scales or null
     const uint16_t* a_rows;     // down: h [P][I] (sorted rows)
     uint16_t* out;              // gate/up: h [P][I]; down: y_sorted [P][H]
+    uint16_t* gu_out;           // tiled gate/up only, optional: g then u [P][2I] (bf16), for the backward
 };
 hipError_t launch_gate_up_skinny(const FfnArgs& a, hipStream_t s);
 hipError_t launch_down_skinny(const FfnArgs& a, hipStream_t s);
@@ -56,6 +57,23 @@ hipError_t launch_down_tiled(const FfnArgs& a, hipStream_t s);
 // ------------------------------------------------------------------ combine
 hipError_t launch_combine(int T, int H, int k, const uint16_t* y_sorted, const int32_t* pair_rank,
                           const float* topk_w, uint16_t* y, hipStream_t s);
+
+// ------------------------------------------------------------------ backward
+int backward_pad_rows(int P, int E);  // rows of the per-expert padded segment buffers
+hipError_t launch_zero_f32(float* p, long long n, hipStream_t s);
+hipError_t launch_transpose_batched(const uint16_t* in, uint16_t* out, int nb, int R, int C, hipStream_t s);
+hipError_t launch_pad_offsets(const int32_t* offsets, int E, int32_t* padoff, uint16_t* dlT, hipStream_t s);
+hipError_t launch_transpose_segments(const uint16_t* in, int C, bool gather, const int32_t* offsets,
+                                     const int32_t* padoff, const int32_t* sorted_pairs, int k, int P, int E,
+                                     uint16_t* out, hipStream_t s);
+hipError_t launch_wgrad(const uint16_t* A, const uint16_t* B, const int32_t* padoff, int E, int M, int N, float* C,
+                        hipStream_t s);
+hipError_t launch_combine_bwd(int P, int H, int k, const uint16_t* dy, const uint16_t* ys, const int32_t* sorted_pairs,
+                              const float* topk_w, uint16_t* dO, float* dw, hipStream_t s);
+hipError_t launch_swiglu_bwd(int P, int I, const uint16_t* da, const uint16_t* gu, uint16_t* dgu, hipStream_t s);
+hipError_t launch_router_bwd(int T, int H, int k, const uint16_t* wr, const int32_t* topk_idx, const float* topk_w,
+                             const float* dw, const int32_t* pair_rank, const int32_t* offsets, const int32_t* padoff,
+                             const uint16_t* dxp, uint16_t* dlT, uint16_t* dx, hipStream_t s);
 
 // ------------------------------------------------------------------ MXFP4 quantiser
 // w bf16 [n_elems] (n_elems % 32 == 0) -> packed [n_elems/2] + scales
