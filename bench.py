@@ -18,7 +18,8 @@ Prints ONE JSON line.  Besides the headline fields it carries:
                 decode and prefill, the 120b token sweep): us per layer,
                 tokens/s and their roofline fractions; and the MXFP4
                 quantiser / fake quantiser on the 20b gate/up tensor (GB/s
-                against the HBM peak).
+                against the HBM peak); and the layer backward on the 20b
+                prefill config (TFLOP/s against the bf16 MFMA peak).
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary]
 
 Traffic measurement (two rocprofv3 counter runs, then a summary):
@@ -340,6 +341,52 @@ def bench_quantize(steps: int):
     return out
 
 
+def bench_backward(steps: int, name: str = "20b_prefill_zipf"):
+    """moe_backward (forward recompute + all gradients) on a prefill config,
+    dy ~ N(0, 1) bf16.  FLOP count: the six expert GEMMs, 18 * P * H * I
+    (forward recompute 6, data gradients 6, weight gradients 6)."""
+    import numpy as np
+    import torch
+
+    import mixture_experts_ffn_05_amd as moe
+    import synth
+    from tests.gpu_layer import to_dev
+    layer = synth.make_layer(name)
+    c = layer.cfg
+    P = c.T * c.k
+    d = moe.dims(c.T, c.H, c.E, c.k, c.I)
+    nbytes = moe.moe_backward_workspace_size(d)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    x, wr = to_dev(layer.x), to_dev(layer.w_router)
+    gu, dn = to_dev(layer.weights.gate_up), to_dev(layer.weights.down)
+    W = moe.expert_weights(gu, dn)
+    dy = to_dev(synth.bf16_from_f32(np.random.default_rng(c.seed + 9).standard_normal((c.T, c.H))
+                                    .astype(np.float32)))
+    dx = torch.empty((c.T, c.H), dtype=torch.int16, device="cuda")
+    dwr = torch.empty((c.E, c.H), dtype=torch.float32, device="cuda")
+    dgu = torch.empty((c.E, 2 * c.I, c.H), dtype=torch.float32, device="cuda")
+    ddn = torch.empty((c.E, c.H, c.I), dtype=torch.float32, device="cuda")
+    call = lambda: moe.moe_backward(d, x, wr, W, dy, dx, dwr, dgu, ddn, ws, nbytes)  # noqa: E731
+    for _ in range(2):
+        call()
+    torch.cuda.synchronize()
+    reps = max(3, steps // 20)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) * 1e-3 / reps
+    fl = 18.0 * P * c.H * c.I
+    out = {"workload": name, "tokens": c.T, "us_per_backward": round(sec * 1e6, 1),
+           "tokens_per_s": round(c.T / sec, 1), "tflops": round(fl / sec / 1e12, 2),
+           "mfma_bf16_frac": round(fl / sec / 1e12 / BF16_PEAK_TFLOPS, 4)}
+    del ws, x, wr, gu, dn, dy, dx, dwr, dgu, ddn
+    torch.cuda.empty_cache()
+    return out
+
+
 def secondary(steps, graph=False):
     import synth
     out = {}
@@ -377,6 +424,7 @@ def secondary(steps, graph=False):
         del tm, layer
     out["120b_sweep"] = sweep
     out["mxfp4_quantize_20b_gate_up"] = bench_quantize(steps)
+    out["backward_20b_prefill_zipf"] = bench_backward(steps)
     return out
 
 
@@ -411,6 +459,9 @@ def main():
     moe.library()
     torch.cuda.set_device(0)
 
+    if args.only == "backward":
+        print(json.dumps(bench_backward(args.steps)))
+        return
     if args.only == "mxfp4_quantize":
         rec = {"workload": args.only, **bench_quantize(args.steps)}
         rec["traffic_bytes_per_launch"] = measured_traffic("mxfp4_quantize")
