@@ -16,21 +16,14 @@
 //   - the weight gradients contract over an expert's tokens, so the sorted
 //     activation rows of each expert segment are transposed into a
 //     zero-padded [rows][Kpad_e] block (transpose_segments_kernel, Kpad_e =
-//     segment length rounded up to 64) and wgrad_kernel multiplies them per
-//     expert.
+//     segment length rounded up to 64) and the tiled kernel's weight-gradient
+//     mode multiplies them per expert.
 // Everything else (combine backward, SwiGLU backward, router backward and dx)
 // is elementwise or a row reduction.
 #include "moe_device.h"
 #include "moe_kernels.h"
 
 namespace moe {
-
-typedef __attribute__((ext_vector_type(16))) float f32x16;
-
-__device__ __forceinline__ f32x16 mfma32x32(bf16x8 a, bf16x8 b, f32x16 c)
-{
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
 
 // ------------------------------------------------------------------ transposes
 
@@ -137,108 +130,6 @@ __global__ __launch_bounds__(WAVE) void pad_offsets_kernel(const int32_t* __rest
         run = __shfl(ex + kp, WAVE - 1, WAVE);
     }
     if (lane == 0) padoff[E] = run;
-}
-
-// ------------------------------------------------------------------ weight-gradient GEMM
-
-constexpr int WG_BM = 128, WG_BN = 128, WG_BK = 32, WG_THREADS = 256;
-constexpr int WG_LD = WG_BK + 8;  // LDS row stride (bf16): 80 B, 16-byte aligned rows
-
-// C[e][m][n] = sum_{j < Kpad_e} A_e[m][j] * B_e[n][j] (fp32 out [E][M][N]);
-// A_e = A + M * padoff[e] ([M][Kpad_e]), B_e = B + N * padoff[e]
-// ([N][Kpad_e]).  Grid: (ceil(N/128), ceil(M/128), E).  Four waves, each
-// 64 x 64 of the tile as 2 x 2 blocks of v_mfma_f32_32x32x16_bf16.  An
-// expert without tokens writes zeros.
-__global__ __launch_bounds__(WG_THREADS) void wgrad_kernel(const uint16_t* __restrict__ A,
-                                                          const uint16_t* __restrict__ B,
-                                                          const int32_t* __restrict__ padoff, int M, int N,
-                                                          float* __restrict__ Cout)
-{
-    __shared__ __attribute__((aligned(16))) uint16_t As[2][WG_BM * WG_LD];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][WG_BN * WG_LD];
-    const int e = blockIdx.z;
-    const int m0 = blockIdx.y * WG_BM, n0 = blockIdx.x * WG_BN;
-    const int p0 = padoff[e], Kpad = padoff[e + 1] - p0;
-    const uint16_t* Ae = A + (size_t)M * p0;
-    const uint16_t* Be = B + (size_t)N * p0;
-    const int t = threadIdx.x, wave = t / WAVE, lane = lane_id();
-    const int wm = (wave & 1) * 64, wn = (wave >> 1) * 64;
-
-    // loads of one K-tile: 2 vectors of 8 per thread per operand
-    u32x4 ra[2], rb[2];
-    auto fetch = [&](int k0) {
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int v = t + WG_THREADS * q;
-            const int i = v >> 2, kv = (v & 3) * 8;
-            ra[q] = m0 + i < M ? *reinterpret_cast<const u32x4*>(Ae + (size_t)(m0 + i) * Kpad + k0 + kv)
-                               : u32x4{0, 0, 0, 0};
-            rb[q] = n0 + i < N ? *reinterpret_cast<const u32x4*>(Be + (size_t)(n0 + i) * Kpad + k0 + kv)
-                               : u32x4{0, 0, 0, 0};
-        }
-    };
-    auto store = [&](int buf) {
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int v = t + WG_THREADS * q;
-            const int i = v >> 2, kv = (v & 3) * 8;
-            *reinterpret_cast<u32x4*>(&As[buf][i * WG_LD + kv]) = ra[q];
-            *reinterpret_cast<u32x4*>(&Bs[buf][i * WG_LD + kv]) = rb[q];
-        }
-    };
-
-    f32x16 acc[2][2];
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
-
-    const int nk = Kpad / WG_BK;
-    if (nk > 0) {
-        fetch(0);
-        store(0);
-        __syncthreads();
-        for (int kt = 0; kt < nk; ++kt) {
-            const int buf = kt & 1;
-            if (kt + 1 < nk) fetch((kt + 1) * WG_BK);
-#pragma unroll
-            for (int ks = 0; ks < WG_BK / 16; ++ks) {
-                const int kk = 16 * ks + 8 * (lane >> 5);
-                bf16x8 fa[2], fb[2];
-#pragma unroll
-                for (int a = 0; a < 2; ++a)
-                    fa[a] = as_bf16x8(*reinterpret_cast<const u32x4*>(&As[buf][(wm + 32 * a + (lane & 31)) * WG_LD + kk]));
-#pragma unroll
-                for (int b = 0; b < 2; ++b)
-                    fb[b] = as_bf16x8(*reinterpret_cast<const u32x4*>(&Bs[buf][(wn + 32 * b + (lane & 31)) * WG_LD + kk]));
-#pragma unroll
-                for (int a = 0; a < 2; ++a)
-#pragma unroll
-                    for (int b = 0; b < 2; ++b) acc[a][b] = mfma32x32(fa[a], fb[b], acc[a][b]);
-            }
-            if (kt + 1 == nk) mfma_drain();
-            // buf ^ 1 was last read in the previous step, which every thread
-            // finished before that step's barrier
-            if (kt + 1 < nk) {
-                store(buf ^ 1);
-                __syncthreads();
-            }
-        }
-    }
-    // epilogue: lane holds column wn + 32b + lane%32, rows wm + 32a + 8(r/4) + 4(lane/32) + r%4
-    float* Ce = Cout + (size_t)e * M * N;
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            const int n = n0 + wn + 32 * b + (lane & 31);
-            if (n >= N) continue;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int m = m0 + wm + 32 * a + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                if (m < M) Ce[(size_t)m * N + n] = acc[a][b][r];
-            }
-        }
 }
 
 // ------------------------------------------------------------------ elementwise / reductions
@@ -418,14 +309,6 @@ hipError_t launch_transpose_segments(const uint16_t* in, int C, bool gather, con
     else
         hipLaunchKernelGGL(transpose_segments_kernel<false>, grid, dim3(TR_THREADS), 0, s, in, C, offsets, padoff,
                            sorted_pairs, k, E, out);
-    return hipGetLastError();
-}
-
-hipError_t launch_wgrad(const uint16_t* A, const uint16_t* B, const int32_t* padoff, int E, int M, int N, float* C,
-                        hipStream_t s)
-{
-    const dim3 grid((N + WG_BN - 1) / WG_BN, (M + WG_BM - 1) / WG_BM, E);
-    hipLaunchKernelGGL(wgrad_kernel, grid, dim3(WG_THREADS), 0, s, A, B, padoff, M, N, C);
     return hipGetLastError();
 }
 

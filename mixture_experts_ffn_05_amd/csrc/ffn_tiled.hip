@@ -35,6 +35,8 @@
 // weight rows; block b works on tile (b % 8) * ceil(tiles / 8) + b / 8 so that
 // the blocks resident on one XCD (dispatched round-robin by block index) take
 // a contiguous run of tiles and share its L2.
+#include <string.h>
+
 #include <type_traits>
 
 #include "moe_device.h"
@@ -146,27 +148,71 @@ __device__ __forceinline__ long long gm_wrow(const FfnArgs& a, int e, int n0, in
     }
 }
 
-template <int WFMT, bool GATE_UP>
+// WGRAD (with WFMT = 0, GATE_UP = false): the weight-gradient product of the
+// backward, C[e][m][n] = sum_j A_e[m][j] B_e[n][j] over expert e's padded
+// segment (Kpad_e a multiple of 64, zero-padded), A_e in the weight role (256
+// rows m per tile) and B_e in the token role (256 rows n per tile); tiles
+// enumerate (expert, m-tile, n-tile) in the same banded, XCD-grouped order.
+template <int WFMT, bool GATE_UP, bool WGRAD>
 __global__ __launch_bounds__(GM_THREADS, GM_WAVES / 4) void gemm_kernel(FfnArgs a)
 {
+    static_assert(!WGRAD || (WFMT == 0 && !GATE_UP), "weight-gradient mode is bf16, no gate/up pairing");
     __shared__ __attribute__((aligned(16))) GmShared sh;
-    const int NOUT = GATE_UP ? a.I : a.H;  // output columns
-    const int K = GATE_UP ? a.H : a.I;
+    const int NOUT = WGRAD ? a.wg_M : (GATE_UP ? a.I : a.H);  // output columns (WGRAD: A rows)
+    int K = GATE_UP ? a.H : a.I;
     const int WCOLS = GATE_UP ? GM_BW / 2 : GM_BW;  // output columns per tile
     const int nt = (NOUT + WCOLS - 1) / WCOLS;
 
     // ---- tile of this block
-    const int total = gm_total_tiles(a.offsets, a.E, nt);
-    const int per = (total + 7) / 8;
-    if ((int)blockIdx.x / 8 >= per) return;  // uniform per block
-    const int tile = (blockIdx.x % 8) * per + blockIdx.x / 8;
-    if (tile >= total) return;
-    int local, mtiles;
-    const int e = gm_locate(a.offsets, a.E, nt, tile, &local, &mtiles);
+    int total, e, local, mtiles;
+    if constexpr (WGRAD) {
+        mtiles = (a.wg_N + GM_BT - 1) / GM_BT;  // token-role tiles
+        total = a.E * mtiles * nt;
+    } else {
+        total = gm_total_tiles(a.offsets, a.E, nt);
+    }
+    [[maybe_unused]] const int tile_w = (int)blockIdx.x;
+    if constexpr (WGRAD) {
+        // Experts' K differ (their token counts) while each has the same
+        // number of tiles, so tiles go out longest first: block b takes tile
+        // b % tpe of the expert ranked b / tpe by descending K (ties: lower
+        // index first).  Consecutive blocks land on different XCDs, so every
+        // expert's tiles spread over the whole chip.
+        if (tile_w >= total) return;  // uniform per block
+        const int tpe = mtiles * nt;
+        const int rank = (int)blockIdx.x / tpe;
+        local = (int)blockIdx.x % tpe;
+        e = -1;
+        for (int base = 0; base < a.E && e < 0; base += WAVE) {
+            const int me = base + lane_id();
+            const int kme = me < a.E ? a.wg_padoff[me + 1] - a.wg_padoff[me] : -1;
+            int r = 0;
+            for (int o = 0; o < a.E; ++o) {
+                const int ko = a.wg_padoff[o + 1] - a.wg_padoff[o];
+                r += (ko > kme || (ko == kme && o < me)) ? 1 : 0;
+            }
+            const uint64_t hit = ballot(me < a.E && r == rank);
+            if (hit) e = base + (int)__builtin_ctzll(hit);
+        }
+    } else {
+        const int per = (total + 7) / 8;
+        if ((int)blockIdx.x / 8 >= per) return;  // uniform per block
+        const int tile = (blockIdx.x % 8) * per + blockIdx.x / 8;
+        if (tile >= total) return;
+        e = gm_locate(a.offsets, a.E, nt, tile, &local, &mtiles);
+    }
     int mt, ntile;
     gm_band(local, mtiles, nt, &mt, &ntile);
-    const int seg1 = a.offsets[e + 1];
-    const int sbase = a.offsets[e] + mt * GM_BT;
+    int seg1 = 0, sbase = 0, p0 = 0;
+    if constexpr (WGRAD) {
+        p0 = a.wg_padoff[e];
+        K = a.wg_padoff[e + 1] - p0;
+        sbase = mt * GM_BT;  // first token-role row (a row of B_e)
+        seg1 = a.wg_N;
+    } else {
+        seg1 = a.offsets[e + 1];
+        sbase = a.offsets[e] + mt * GM_BT;
+    }
     const int n0 = ntile * WCOLS;
 
     const int tid = threadIdx.x, lane = lane_id(), wave = tid / WAVE;
@@ -187,6 +233,12 @@ __global__ __launch_bounds__(GM_THREADS, GM_WAVES / 4) void gemm_kernel(FfnArgs 
         const int row = 16 * (wave + GM_WAVES * i) + lrow;
         lchunk[i] = lpc ^ ((row >> 2) & 3);
         const int s = sbase + row;
+        if constexpr (WGRAD) {
+            xsrc[i] = a.wg_b + (size_t)a.wg_N * p0 + (size_t)(s < seg1 ? s : 0) * K;
+            const int m = n0 + row;
+            wsrc[i] = a.wg_a + (size_t)a.wg_M * p0 + (size_t)(m < NOUT ? m : 0) * K;
+            continue;
+        }
         if constexpr (GATE_UP)
             xsrc[i] = a.x + (size_t)(s < seg1 ? a.sorted_pairs[s] / a.k : 0) * a.H;
         else
@@ -289,6 +341,8 @@ __global__ __launch_bounds__(GM_THREADS, GM_WAVES / 4) void gemm_kernel(FfnArgs 
     // first fragments are read.  Direct loads run GM_DIST stages ahead, MXFP4
     // register loads two.  Per stage a wave issues, in order: the register
     // loads of stage st+3, (barrier), the direct loads of stage st+3.
+    // (an expert without tokens in the weight-gradient mode has no K: its tile is zero)
+    if (!WGRAD || nstages > 0) {
     for (int st = 0; st < GM_DIST; ++st) issue(st);
     if constexpr (WFMT == 1) {
         fetch_q(0, 0);
@@ -338,6 +392,24 @@ __global__ __launch_bounds__(GM_THREADS, GM_WAVES / 4) void gemm_kernel(FfnArgs 
     mma(f1);
     mfma_drain();
     vm_wait<0>();  // the surplus loads past the last stage
+    }
+
+    if constexpr (WGRAD) {  // fp32 C[e][m][n]: m = weight-role row, n = token-role row
+        float* C = a.wg_out + (size_t)e * a.wg_M * a.wg_N;
+#pragma unroll
+        for (int t = 0; t < GM_TB; ++t) {
+            const int ncol = sbase + 32 * GM_TB * wt + 32 * t + r32;
+            if (ncol >= a.wg_N) continue;
+#pragma unroll
+            for (int m = 0; m < GM_WB; ++m)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int mrow = n0 + 128 * ww + 32 * m + 8 * (r >> 2) + 4 * kg + (r & 3);
+                    if (mrow < NOUT) C[(size_t)mrow * a.wg_N + ncol] = acc[m][t][r];
+                }
+        }
+        return;
+    }
 
     // ---- epilogue: for each (m, t) the lane holds tile weight rows
     // 128ww + 32m + 8(r/4) + 4(lane/32) + r%4 (r = 0..15) of token
@@ -398,7 +470,7 @@ static hipError_t launch_gemm(const FfnArgs& a, hipStream_t s)
     const long long mt_bound = ((long long)a.T * a.k + GM_BT - 1) / GM_BT + a.E;
     long long grid = nt * mt_bound;
     grid = (grid + 7) / 8 * 8;
-    hipLaunchKernelGGL((gemm_kernel<WFMT, GATE_UP>), dim3((unsigned)grid), dim3(GM_THREADS), 0, s, a);
+    hipLaunchKernelGGL((gemm_kernel<WFMT, GATE_UP, false>), dim3((unsigned)grid), dim3(GM_THREADS), 0, s, a);
     return hipGetLastError();
 }
 
@@ -410,6 +482,23 @@ hipError_t launch_gate_up_tiled(const FfnArgs& a, hipStream_t s)
 hipError_t launch_down_tiled(const FfnArgs& a, hipStream_t s)
 {
     return a.wfmt == 0 ? launch_gemm<0, false>(a, s) : launch_gemm<1, false>(a, s);
+}
+
+hipError_t launch_wgrad_tiled(const uint16_t* A, const uint16_t* B, const int32_t* padoff, int E, int M, int N,
+                              float* C, hipStream_t s)
+{
+    FfnArgs a;
+    memset(&a, 0, sizeof a);
+    a.E = E;
+    a.wg_a = A;
+    a.wg_b = B;
+    a.wg_padoff = padoff;
+    a.wg_M = M;
+    a.wg_N = N;
+    a.wg_out = C;
+    const long long grid = (long long)E * ((M + GM_BW - 1) / GM_BW) * ((N + GM_BT - 1) / GM_BT);
+    hipLaunchKernelGGL((gemm_kernel<0, false, true>), dim3((unsigned)grid), dim3(GM_THREADS), 0, s, a);
+    return hipGetLastError();
 }
 
 }  // namespace moe

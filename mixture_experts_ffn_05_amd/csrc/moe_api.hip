@@ -331,9 +331,9 @@ int moe_backward(const moe_dims* dims, const void* x, const void* w_router, cons
     if ((rc = hip_status(moe::launch_transpose_segments(dgu, 2 * I, false, off, padoff, sp, d.k, P, E, dguT, s))))
         return rc;
     if ((rc = hip_status(moe::launch_transpose_segments(xb, H, true, off, padoff, sp, d.k, P, E, xT, s)))) return rc;
-    if ((rc = hip_status(moe::launch_wgrad(dOT, hT, padoff, E, H, I, ddown, s)))) return rc;
-    if ((rc = hip_status(moe::launch_wgrad(dguT, xT, padoff, E, 2 * I, H, dgate_up, s)))) return rc;
-    return hip_status(moe::launch_wgrad(dlT, xT, padoff, E, 1, H, dw_router, s));
+    if ((rc = hip_status(moe::launch_wgrad_tiled(dOT, hT, padoff, E, H, I, ddown, s)))) return rc;
+    if ((rc = hip_status(moe::launch_wgrad_tiled(dguT, xT, padoff, E, 2 * I, H, dgate_up, s)))) return rc;
+    return hip_status(moe::launch_wgrad_tiled(dlT, xT, padoff, E, 1, H, dw_router, s));
 }
 
 int moe_workspace_size(const moe_dims* dims, size_t* bytes)

@@ -48,6 +48,13 @@ struct FfnArgs {
     const uint16_t* a_rows;     // down: h [P][I] (sorted rows)
     uint16_t* out;              // gate/up: h [P][I]; down: y_sorted [P][H]
     uint16_t* gu_out;           // tiled gate/up only, optional: g then u [P][2I] (bf16), for the backward
+    // weight-gradient mode of the tiled kernel: C[e][m][n] = sum_j A_e[m][j] B_e[n][j]
+    // (fp32), A_e = wg_a + wg_M * padoff[e] ([wg_M][Kpad_e]), B_e likewise with wg_N
+    const uint16_t* wg_a;
+    const uint16_t* wg_b;
+    const int32_t* wg_padoff;   // [E+1]
+    int wg_M, wg_N;
+    float* wg_out;              // [E][wg_M][wg_N]
 };
 hipError_t launch_gate_up_skinny(const FfnArgs& a, hipStream_t s);
 hipError_t launch_down_skinny(const FfnArgs& a, hipStream_t s);
@@ -66,8 +73,8 @@ hipError_t launch_pad_offsets(const int32_t* offsets, int E, int32_t* padoff, ui
 hipError_t launch_transpose_segments(const uint16_t* in, int C, bool gather, const int32_t* offsets,
                                      const int32_t* padoff, const int32_t* sorted_pairs, int k, int P, int E,
                                      uint16_t* out, hipStream_t s);
-hipError_t launch_wgrad(const uint16_t* A, const uint16_t* B, const int32_t* padoff, int E, int M, int N, float* C,
-                        hipStream_t s);
+hipError_t launch_wgrad_tiled(const uint16_t* A, const uint16_t* B, const int32_t* padoff, int E, int M, int N,
+                              float* C, hipStream_t s);
 hipError_t launch_combine_bwd(int P, int H, int k, const uint16_t* dy, const uint16_t* ys, const int32_t* sorted_pairs,
                               const float* topk_w, uint16_t* dO, float* dw, hipStream_t s);
 hipError_t launch_swiglu_bwd(int P, int I, const uint16_t* da, const uint16_t* gu, uint16_t* dgu, hipStream_t s);
