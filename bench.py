@@ -19,7 +19,9 @@ Prints ONE JSON line.  Besides the headline fields it carries:
                 tokens/s and their roofline fractions; and the MXFP4
                 quantiser / fake quantiser on the 20b gate/up tensor (GB/s
                 against the HBM peak); and the layer backward on the 20b
-                prefill config (TFLOP/s against the bf16 MFMA peak).
+                prefill config (TFLOP/s against the bf16 MFMA peak); and MXFP4
+                decode with the expert weights in pinned host memory (GB/s
+                against the host link).
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary]
 
 Traffic measurement (two rocprofv3 counter runs, then a summary):
@@ -387,6 +389,44 @@ def bench_backward(steps: int, name: str = "20b_prefill_zipf"):
     return out
 
 
+HOST_LINK_GBS = 64.0  # PCIe Gen5 x16, one direction
+
+
+def bench_host_weights(name: str = "20b_mxfp4_decode", reps: int = 5):
+    """Decode with the expert weights in pinned host memory (mapped; the skinny
+    kernels read only the touched experts' rows over the host link): us per
+    layer and GB/s of touched weight bytes against the link's peak."""
+    import torch
+
+    import mixture_experts_ffn_05_amd as moe
+    import synth
+    from tests.gpu_layer import GpuLayer
+    from tests.host_weights import pinned_weights
+    layer = synth.make_layer(name)
+    g = GpuLayer(layer)
+    parts = pinned_weights(layer.weights)
+    if parts is None:
+        return {"workload": name, "skipped": "pinned host memory not mapped"}
+    ptrs = [p.dev for p in parts] + [None, None]
+    g.weights = moe.expert_weights(ptrs[0], ptrs[1], ptrs[2], ptrs[3])
+    g.forward()
+    torch.cuda.synchronize()
+    touched = int(torch.unique(g.topk_idx).numel())  # moe_forward writes the routing when asked
+    total_b, gu_b = layer_bytes(layer.cfg, touched)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.forward()
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) * 1e-3 / reps
+    del g, parts
+    torch.cuda.empty_cache()
+    return {"workload": name, "us_per_layer": round(sec * 1e6, 1), "touched_experts": touched,
+            "gbs": round(total_b / sec / 1e9, 2), "link_peak_gbs": HOST_LINK_GBS,
+            "link_frac": round(total_b / sec / 1e9 / HOST_LINK_GBS, 4), "gate_up_bytes": int(gu_b)}
+
+
 def secondary(steps, graph=False):
     import synth
     out = {}
@@ -425,6 +465,7 @@ def secondary(steps, graph=False):
     out["120b_sweep"] = sweep
     out["mxfp4_quantize_20b_gate_up"] = bench_quantize(steps)
     out["backward_20b_prefill_zipf"] = bench_backward(steps)
+    out["host_weights_20b_mxfp4_decode"] = bench_host_weights("20b_mxfp4_decode")
     return out
 
 
@@ -459,6 +500,9 @@ def main():
     moe.library()
     torch.cuda.set_device(0)
 
+    if args.only == "host_weights":
+        print(json.dumps([bench_host_weights("20b_mxfp4_decode"), bench_host_weights("20b_decode")]))
+        return
     if args.only == "backward":
         print(json.dumps(bench_backward(args.steps)))
         return

@@ -55,6 +55,12 @@
  *   y_sorted       bf16  [P][H]   unweighted expert outputs, row s = sorted position
  *   y              bf16  [T][H]
  *
+ * Expert weights may also live in pinned host memory, passed as the device
+ * address of the mapping (hipHostGetDevicePointer): in the skinny regime the
+ * kernels then read only the touched experts' rows over the host link, once
+ * per layer (the pinned-host-bank streaming that the pages' serving engines
+ * use for models larger than the GPU's memory; "gpt-oss-20b" model page).
+ *
  * Alignment: bf16 matrices, weight bytes and the workspace must be 16-byte
  * aligned; int32/fp32 arrays 4-byte aligned; scale arrays need no alignment.
  * Supported sizes: 1 <= E <= 256, 1 <= k <= min(E, 8), H and I multiples of

@@ -1,0 +1,51 @@
+"""Expert weights in pinned host memory, for the host-streamed decode path.
+
+The pages describe serving engines that keep expert weights in pinned host
+memory and stream them to the GPU, which pays off only for models larger
+than the GPU's memory ("gpt-oss-20b" model page: the 12 GB model fits one
+16 GB card, so keeping every expert resident is faster than streaming them
+from pinned host banks).  The library takes plain pointers, so its skinny
+kernels read such weights directly: only the touched experts' rows cross the
+host link, each once per layer.
+
+Here: torch's pinned allocation (hipHostMalloc) for the bytes, and the device
+address of that mapping from hipHostGetDevicePointer (the documented
+zero-copy route).  Returns None when the runtime does not map it.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+
+def _hip():
+    lib = ctypes.CDLL(os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
+    lib.hipHostGetDevicePointer.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p, ctypes.c_uint]
+    lib.hipHostGetDevicePointer.restype = ctypes.c_int
+    return lib
+
+
+class PinnedArray:
+    """A host array copied into pinned memory; .dev is its device address."""
+
+    def __init__(self, a: np.ndarray):
+        a = np.ascontiguousarray(a)
+        self.host = torch.empty(a.nbytes, dtype=torch.uint8, pin_memory=True)
+        self.host.numpy()[:] = a.view(np.uint8).reshape(-1)
+        dev = ctypes.c_void_p(0)
+        rc = _hip().hipHostGetDevicePointer(ctypes.byref(dev), ctypes.c_void_p(self.host.data_ptr()), 0)
+        self.dev = dev.value if rc == 0 and dev.value else None
+
+
+def pinned_weights(w):
+    """(gate_up, down, gate_up_scale, down_scale) of a synth.Weights in pinned
+    host memory, or None if any of them cannot be mapped."""
+    parts = [PinnedArray(w.gate_up), PinnedArray(w.down)]
+    if w.wfmt == 1:
+        parts += [PinnedArray(w.gate_up_scale), PinnedArray(w.down_scale)]
+    if any(p.dev is None for p in parts):
+        return None
+    return parts
