@@ -99,3 +99,28 @@ def test_quantizer_argument_errors_launch_nothing(lib):
     # an empty tensor is a no-op that succeeds even with null buffers
     assert q(0, 64, None, None, None, None) == moe.MOE_OK
     assert f(7, 0, None, None, None) == moe.MOE_OK
+
+
+def test_backward_argument_errors_launch_nothing(lib):
+    A = 0x10000  # fake, 16-byte aligned device address: never dereferenced on these paths
+    byref = ctypes.byref
+    d = moe.dims(8, 64, 4, 2, 96)
+    n = moe.moe_backward_workspace_size(d)
+    assert n >= moe.moe_workspace_size(d)  # the backward workspace includes the forward's
+    W = moe.expert_weights(A, A)
+    bwd = lib.moe_backward
+    # MXFP4 weights have no backward
+    d4 = moe.dims(8, 64, 4, 2, 96, wfmt=moe.MOE_WFMT_MXFP4)
+    with pytest.raises(moe.MoeError) as ex:
+        moe.moe_backward_workspace_size(d4)
+    assert ex.value.code == moe.MOE_ERR_UNSUPPORTED
+    assert bwd(byref(d4), A, A, byref(W), A, A, A, A, A, A, n, None) == moe.MOE_ERR_UNSUPPORTED
+    # missing or misaligned gradient outputs, misaligned inputs, small workspace, bad dims
+    assert bwd(byref(d), A, A, byref(W), A, A, None, A, A, A, n, None) == moe.MOE_ERR_INVALID_ARG
+    assert bwd(byref(d), A, A, byref(W), A, A, A + 2, A, A, A, n, None) == moe.MOE_ERR_MISALIGNED
+    assert bwd(byref(d), A + 8, A, byref(W), A, A, A, A, A, A, n, None) == moe.MOE_ERR_MISALIGNED
+    assert bwd(byref(d), A, A, byref(W), A, A + 2, A, A, A, A, n, None) == moe.MOE_ERR_MISALIGNED
+    assert bwd(byref(d), A, A, byref(W), A, A, A, A, A, A, n - 1, None) == moe.MOE_ERR_WORKSPACE
+    dbad = moe.dims(8, 64, 4, 9, 96)
+    assert bwd(byref(dbad), A, A, byref(W), A, A, A, A, A, A, n, None) == moe.MOE_ERR_INVALID_ARG
+    assert bwd(None, A, A, byref(W), A, A, A, A, A, A, n, None) == moe.MOE_ERR_INVALID_ARG
