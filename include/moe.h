@@ -59,7 +59,8 @@
  * address of the mapping (hipHostGetDevicePointer): in the skinny regime the
  * kernels then read only the touched experts' rows over the host link, once
  * per layer (the pinned-host-bank streaming that the pages' serving engines
- * use for models larger than the GPU's memory; "gpt-oss-20b" model page).
+ * use for models larger than the GPU's memory; "gpt-oss-20b" model page,
+ * section "llama-swap.yaml entry").
  *
  * Alignment: bf16 matrices, weight bytes and the workspace must be 16-byte
  * aligned; int32/fp32 arrays 4-byte aligned; scale arrays need no alignment.

@@ -2,9 +2,9 @@
 
 The pages describe serving engines that keep expert weights in pinned host
 memory and stream them to the GPU, which pays off only for models larger
-than the GPU's memory ("gpt-oss-20b" model page: the 12 GB model fits one
-16 GB card, so keeping every expert resident is faster than streaming them
-from pinned host banks).  The library takes plain pointers, so its skinny
+than the GPU's memory ("gpt-oss-20b" model page, section "llama-swap.yaml
+entry": the 12 GB model fits one 16 GB card, so keeping every expert
+resident is faster than streaming them from pinned host banks).  The library takes plain pointers, so its skinny
 kernels read such weights directly: only the touched experts' rows cross the
 host link, each once per layer.
 
