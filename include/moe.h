@@ -168,9 +168,10 @@ int moe_combine(const moe_dims* dims, const void* y_sorted, const int32_t* pair_
 int moe_forward(const moe_dims* dims, const void* x, const void* w_router, const moe_expert_weights* weights, void* y,
                 int32_t* topk_idx_out, float* topk_w_out, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Backward of moe_forward (the training variant: every expert's parameters
- * are fine-tuned in bf16 with fp32 reductions, "Persona Kappa: training a
- * 20B LLM on desktop GPUs", section "Techniques That Made It Fit"), for
+/* Backward of moe_forward (the training variant: full-parameter fine-tuning,
+ * "kappa-20b-131k" model card; bf16 with fp32 accumulation and activations
+ * recomputed during backprop, "Persona Kappa: training a 20B LLM on desktop
+ * GPUs", section "Techniques That Made It Fit"), for
  * bf16 weights (dims->wfmt = MOE_WFMT_BF16, else MOE_ERR_UNSUPPORTED).
  * Given the upstream gradient dy bf16 [T][H] of the layer output y, it
  * recomputes the forward (routing, permutation, gate/up, down) and writes the

@@ -1,6 +1,8 @@
-// Backward of the MoE layer: the training variant (the pages fine-tune every
-// expert's parameters in bf16 with fp32 reductions: "Persona Kappa: training
-// a 20B LLM on desktop GPUs", section "Techniques That Made It Fit").  Given
+// Backward of the MoE layer: the training variant (full-parameter fine-tuning:
+// "kappa-20b-131k" model card; bf16 forward with fp32 accumulation, and
+// activations recomputed during backprop instead of stored: "Persona Kappa:
+// training a 20B LLM on desktop GPUs", section "Techniques That Made It
+// Fit").  The entry point recomputes the forward, keeping g and u.  Given
 // dy = dL/dy, per pair (token t, slot j, expert e) of the forward
 //   dw_j = dy . o_j,   do_j = w_j dy,   da = Wd^T do_j,
 //   dg = da * u * silu'(g),  du = da * silu(g),
