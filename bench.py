@@ -12,7 +12,9 @@ Prints ONE JSON line.  Besides the headline fields it carries:
   roofline      the dominant kernel (gate/up + SwiGLU) against the HBM peak:
                 algorithmic bytes per launch (weights of the experts the
                 routing touched) / its mean duration from HIP events on the
-                launch stream;
+                launch stream; frac_of_copy relates it to hbm_copy_gbs, the
+                bandwidth a plain 1 GiB copy kernel achieves on this GPU;
+  ms_per_step_hip_graph  the same step replayed from a captured HIP graph;
   cpu_baseline  the CPU oracle timed on this host on the whole 16-token layer;
   secondary     the other workloads (prefill bf16 with Zipf routing, MXFP4
                 decode and prefill, the 120b token sweep): us per layer,
@@ -249,6 +251,27 @@ def copy_probe(reps: int = 5):
     for _ in range(reps):
         torch.neg(src, out=dst)
     torch.cuda.synchronize()
+
+
+def copy_bandwidth(reps: int = 10) -> float:
+    """Achievable HBM bandwidth (GB/s) of a plain elementwise copy kernel
+    (torch.neg over a 1 GiB bf16 tensor: 1 GiB read + 1 GiB written), timed
+    with HIP events: the measured counterpart of the datasheet peak."""
+    import torch
+    src = torch.ones(COPY_PROBE_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        torch.neg(src, out=dst)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        torch.neg(src, out=dst)
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) * 1e-3 / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return round(2 * COPY_PROBE_BYTES / sec / 1e9, 1)
 
 
 def _counter_means(run_dir: str, counter: str):
@@ -556,6 +579,11 @@ def main():
                      "traffic": measured_traffic("gate_up_skinny"),
                      "algorithmic_bytes_per_launch": gu_b, "mean_launch_us": round(gu_us, 2)},
     }
+    # the same layer step replayed from a captured HIP graph, for reference (eager launches are the headline)
+    sec_other = tm.run(args.steps, args.warmup, graph=not args.graph)
+    rec["ms_per_step_" + ("eager" if args.graph else "hip_graph")] = round(sec_other * 1e3, 4)
+    rec["hbm_copy_gbs"] = copy_bandwidth()
+    rec["roofline"]["frac_of_copy"] = round(achieved / rec["hbm_copy_gbs"], 4)
     if not args.no_secondary:
         del tm
         torch.cuda.empty_cache()
