@@ -450,9 +450,33 @@ def bench_host_weights(name: str = "20b_mxfp4_decode", reps: int = 5):
             "link_frac": round(total_b / sec / 1e9 / HOST_LINK_GBS, 4), "gate_up_bytes": int(gu_b)}
 
 
+def library_gemm_tflops(M: int = 32768, K: int = 2880, N: int = 5760, reps: int = 10) -> float:
+    """Dense bf16 GEMM of the library torch dispatches to (hipBLASLt/rocBLAS)
+    on random N(0, 1) data with the grouped gate/up's FLOP count (all pairs x
+    one expert's 2I x H): the achievable-MFMA reference point."""
+    import torch
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    a = torch.randn((M, K), generator=g, device="cuda").to(torch.bfloat16)
+    b = torch.randn((K, N), generator=g, device="cuda").to(torch.bfloat16).contiguous()
+    for _ in range(3):
+        c = torch.mm(a, b)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        c = torch.mm(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) * 1e-3 / reps
+    del a, b, c
+    torch.cuda.empty_cache()
+    return round(2.0 * M * K * N / sec / 1e12, 2)
+
+
 def secondary(steps, graph=False):
     import synth
     out = {}
+    out["library_dense_gemm_bf16_tflops"] = library_gemm_tflops()
     # prefill regimes: MFMA-bound
     for name in ("20b_prefill_zipf", "20b_mxfp4_prefill"):
         layer = synth.make_layer(name)
