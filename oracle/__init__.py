@@ -69,6 +69,10 @@ def _bind(lib):
     lib.orc_mxfp4_fakequant.restype = _I
     lib.orc_mxfp4_fakequant.argtypes = [_I64, _I64, _P, _P]
     lib.orc_max_threads.restype = _I
+    lib.orc_mxfp4_pack.argtypes = [_I, _I64, _I64, _I64, _P, _P, _P, _P]
+    lib.orc_mxfp4_pack.restype = _I
+    lib.orc_mxfp4_unpack.argtypes = [_I, _I64, _I64, _I64, _P, _P, _P, _P]
+    lib.orc_mxfp4_unpack.restype = _I
     lib.orc_max_threads.argtypes = []
     return lib
 
@@ -212,6 +216,27 @@ class Oracle:
         out = np.empty((rows, cols), np.uint16)
         self._check(self.lib.orc_mxfp4_fakequant(rows, cols, self._ptr(w), self._ptr(out)), "fakequant")
         return out
+
+    # ------------------------------------------------------------ packed order
+    def _pack_io(self, gate_up: bool, E: int, I: int, H: int, w, s):
+        R, K = (2 * I, H) if gate_up else (H, I)
+        w = np.ascontiguousarray(w, np.uint8).reshape(E, R, K // 2)
+        s = np.ascontiguousarray(s, np.uint8).reshape(E, R, K // 32)
+        return w, s, np.empty_like(w), np.empty_like(s)
+
+    def mxfp4_pack(self, gate_up: bool, E: int, I: int, H: int, w, s):
+        """Row-major MXFP4 expert tensor (bytes, scales) -> the packed order."""
+        w, s, wp, sp = self._pack_io(gate_up, E, I, H, w, s)
+        self._check(self.lib.orc_mxfp4_pack(int(gate_up), E, I, H, self._ptr(w), self._ptr(s), self._ptr(wp),
+                                            self._ptr(sp)), "mxfp4_pack")
+        return wp, sp
+
+    def mxfp4_unpack(self, gate_up: bool, E: int, I: int, H: int, wp, sp):
+        """Packed MXFP4 expert tensor -> row-major (bytes, scales)."""
+        wp, sp, w, s = self._pack_io(gate_up, E, I, H, wp, sp)
+        self._check(self.lib.orc_mxfp4_unpack(int(gate_up), E, I, H, self._ptr(wp), self._ptr(sp), self._ptr(w),
+                                              self._ptr(s)), "mxfp4_unpack")
+        return w, s
 
     def max_threads(self) -> int:
         return self.lib.orc_max_threads()

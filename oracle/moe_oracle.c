@@ -779,6 +779,128 @@ int orc_mxfp4_fakequant(int64_t rows, int64_t cols, const uint16_t* w, uint16_t*
     return ORC_OK;
 }
 
+/* ------------------------------------------------------- packed MXFP4 order
+ *
+ * A storage order for MXFP4 expert weights that this library defines for
+ * decode-time weight streaming.  The pages fix the number format (E2M1 + one
+ * E8M0 scale per 32 elements, "Persona Kappa" post, section "Quantization-
+ * Aware Training (QAT)"), not a byte order; this order keeps every byte and
+ * scale unchanged and only moves them.  Per expert, a piece is the 16 bytes
+ * of one row over one K-block (elements 32kb .. 32kb+31 of the row), and it
+ * carries that block's scale byte.  Rows form items of 32 slots:
+ *   gate/up tensor [2I][K=H]: item i has gate rows 16i..16i+15 in slots
+ *                              0..15 and up rows I+16i..I+16i+15 in 16..31;
+ *   down tensor [H][K=I]:     item i has rows 32i..32i+31 in slots 0..31.
+ * Write slot q = 4g + t (g < 8, t < 4) and K-block kb = 16c + b (chunk c,
+ * b < 16); with nkb = K/32 and nb(c) = min(16, nkb - 16c) blocks in chunk c,
+ * the piece (item i, slot q, kb) sits at byte
+ *     i*512*nkb + c*8192 + g*64*nb(c) + 16*(4b + t)
+ * of the expert's packed bytes and its scale at byte
+ *     i*32*nkb + c*512 + 8*(4b + t) + g
+ * of the expert's packed scales.  Experts follow each other at the same
+ * strides as in the row-major layout (rows*K/2 bytes, rows*K/32 scales).
+ *
+ * orc_mxfp4_pack computes each piece's destination from the formula above;
+ * orc_mxfp4_unpack walks the packed bytes in address order (item, chunk,
+ * then g, b, t for bytes and b, t, g for scales) and derives each source
+ * from the loop position, so the two are independent descriptions of one
+ * permutation. */
+
+/* Row of expert-local slot q of item i (gate_up != 0: paired gate/up rows). */
+static int64_t packed_slot_row(int gate_up, int64_t I, int64_t i, int q)
+{
+    if (!gate_up) return 32 * i + q;
+#if ORC_PLANT == 40
+    return 16 * i + q; /* planted: up rows read from the gate half */
+#else
+    return q < 16 ? 16 * i + q : I + 16 * i + (q - 16);
+#endif
+}
+
+static int packed_args_ok(int gate_up, int64_t E, int64_t I, int64_t H)
+{
+    /* items of 32 rows (gate/up pairs 16 columns of each half) and whole K-blocks */
+    if (E <= 0 || I <= 0 || H <= 0 || (gate_up != 0 && gate_up != 1)) return 0;
+    return gate_up ? I % 16 == 0 && H % 32 == 0 : H % 32 == 0 && I % 32 == 0;
+}
+
+/* gate_up = 1: w u8 [E][2I][H/2], s u8 [E][2I][H/32]; gate_up = 0: w u8
+ * [E][H][I/2], s u8 [E][H][I/32].  Writes wp, sp of the same sizes. */
+int orc_mxfp4_pack(int gate_up, int64_t E, int64_t I, int64_t H, const uint8_t* w, const uint8_t* s, uint8_t* wp,
+                   uint8_t* sp)
+{
+    if (!packed_args_ok(gate_up, E, I, H) || !w || !s || !wp || !sp) return ORC_ERR_ARG;
+    const int64_t R = gate_up ? 2 * I : H, K = gate_up ? H : I, nkb = K / 32;
+    for (int64_t e = 0; e < E; ++e) {
+        const uint8_t* we = w + e * R * (K / 2);
+        const uint8_t* se = s + e * R * nkb;
+        uint8_t* wpe = wp + e * R * (K / 2);
+        uint8_t* spe = sp + e * R * nkb;
+        for (int64_t r = 0; r < R; ++r) {
+            int64_t i;
+            int q;
+            if (gate_up) {
+                const int64_t n = r < I ? r : r - I; /* output column of the row */
+                i = n / 16;
+                q = (int)(n % 16) + (r < I ? 0 : 16);
+            } else {
+                i = r / 32;
+                q = (int)(r % 32);
+            }
+            const int g = q / 4, t = q % 4;
+            for (int64_t kb = 0; kb < nkb; ++kb) {
+                const int64_t c = kb / 16, b = kb % 16;
+                const int64_t nb = nkb - 16 * c < 16 ? nkb - 16 * c : 16;
+#if ORC_PLANT == 41
+                const int64_t dst = i * 512 * nkb + c * 512 * nb + g * 64 * nb + 16 * (4 * b + t); /* planted: chunk base from its own width */
+#else
+                const int64_t dst = i * 512 * nkb + c * 8192 + g * 64 * nb + 16 * (4 * b + t);
+#endif
+                memcpy(wpe + dst, we + r * (K / 2) + 16 * kb, 16);
+                spe[i * 32 * nkb + c * 512 + 8 * (4 * b + t) + g] = se[r * nkb + kb];
+            }
+        }
+    }
+    return ORC_OK;
+}
+
+/* Inverse of orc_mxfp4_pack (same arguments, packed in, row-major out). */
+int orc_mxfp4_unpack(int gate_up, int64_t E, int64_t I, int64_t H, const uint8_t* wp, const uint8_t* sp, uint8_t* w,
+                     uint8_t* s)
+{
+    if (!packed_args_ok(gate_up, E, I, H) || !w || !s || !wp || !sp) return ORC_ERR_ARG;
+    const int64_t R = gate_up ? 2 * I : H, K = gate_up ? H : I, nkb = K / 32;
+    const int64_t items = R / 32, chunks = (nkb + 15) / 16;
+    const uint8_t* src = wp;
+    const uint8_t* ssrc = sp;
+    for (int64_t e = 0; e < E; ++e) {
+        uint8_t* we = w + e * R * (K / 2);
+        uint8_t* se = s + e * R * nkb;
+        for (int64_t i = 0; i < items; ++i)
+            for (int64_t c = 0; c < chunks; ++c) {
+                const int64_t nb = nkb - 16 * c < 16 ? nkb - 16 * c : 16;
+                for (int g = 0; g < 8; ++g)
+                    for (int64_t b = 0; b < nb; ++b)
+                        for (int t = 0; t < 4; ++t) {
+                            const int64_t r = packed_slot_row(gate_up, I, i, 4 * g + t);
+                            memcpy(we + r * (K / 2) + 16 * (16 * c + b), src, 16);
+                            src += 16;
+                        }
+                for (int64_t b = 0; b < nb; ++b)
+                    for (int t = 0; t < 4; ++t)
+                        for (int g = 0; g < 8; ++g) {
+#if ORC_PLANT == 42
+                            const int64_t r = packed_slot_row(gate_up, I, i, 4 * t + g % 4); /* planted: slot from (t, g) swapped */
+#else
+                            const int64_t r = packed_slot_row(gate_up, I, i, 4 * g + t);
+#endif
+                            se[r * nkb + 16 * c + b] = *ssrc++;
+                        }
+            }
+    }
+    return ORC_OK;
+}
+
 /* Threads the OpenMP runtime will use for a parallel region (1 without it). */
 int orc_max_threads(void)
 {

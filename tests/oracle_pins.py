@@ -23,7 +23,10 @@ What pins what:
     matmuls, non-square H != I so a transposed operand shows), in bf16 and in
     MXFP4 (decoded independently from the golden E2M1 table), identical
     experts, k=E mixture, per-token independence, linearity in W_down,
-    silu(0)=0, and a whole layer worked by hand.
+    silu(0)=0, and a whole layer worked by hand;
+  - packed MXFP4 order: hand-worked piece and scale positions
+    (tests/golden/mxfp4_packed_positions.txt) and pack/unpack inverse both
+    ways, unpack being an independent address-order walk.
 """
 from __future__ import annotations
 
@@ -586,6 +589,39 @@ def pin_hand_layer(o):
     assert list(idx[0]) == [int(v) for v in g["topk_idx"]]
     _close(w[0], g["topk_w"], rtol=1e-15, atol=0)
     _close(y[0], g["y"], rtol=1e-14, atol=0)
+
+
+# --------------------------------------------------------------------------- packed MXFP4 order
+
+
+def _packed_tensor(seed, gate_up, E, I, H):
+    R, K = (2 * I, H) if gate_up else (H, I)
+    rng = np.random.default_rng(seed)
+    return (rng.integers(0, 256, (E, R, K // 2), dtype=np.uint8), rng.integers(0, 256, (E, R, K // 32), dtype=np.uint8))
+
+
+def pin_packed_hand_positions(o):
+    """Pieces land where the hand-worked fixture puts them."""
+    for kind, E, I, H, e, r, kb, off, soff in _golden_rows("mxfp4_packed_positions.txt"):
+        gate_up = kind == "gu"
+        E, I, H, e, r, kb, off, soff = (int(v) for v in (E, I, H, e, r, kb, off, soff))
+        w, s = _packed_tensor(7, gate_up, E, I, H)
+        wp, sp = o.mxfp4_pack(gate_up, E, I, H, w, s)
+        assert np.array_equal(wp.reshape(-1)[off:off + 16], w[e, r, 16 * kb:16 * kb + 16]), (kind, e, r, kb)
+        assert sp.reshape(-1)[soff] == s[e, r, kb], (kind, e, r, kb)
+
+
+def pin_packed_round_trip(o):
+    """pack and unpack are inverse permutations, over K-block counts below,
+    at and across one chunk (1, 3, 16, 17, 90) and both tensor kinds."""
+    for gate_up, E, I, H in [(True, 2, 16, 32), (True, 1, 32, 96), (False, 2, 64, 512), (False, 1, 544, 32),
+                             (True, 1, 48, 2880), (False, 1, 2880, 64)]:
+        w, s = _packed_tensor(11, gate_up, E, I, H)
+        wp, sp = o.mxfp4_pack(gate_up, E, I, H, w, s)
+        w2, s2 = o.mxfp4_unpack(gate_up, E, I, H, wp, sp)
+        assert np.array_equal(w2, w) and np.array_equal(s2, s), (gate_up, E, I, H)
+        w3, s3 = o.mxfp4_pack(gate_up, E, I, H, *o.mxfp4_unpack(gate_up, E, I, H, w, s))
+        assert np.array_equal(w3, w) and np.array_equal(s3, s), (gate_up, E, I, H)
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

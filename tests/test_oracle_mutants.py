@@ -7,7 +7,9 @@ swapped, 6 silu sign error, 7 routing weights not normalised, 20 quantizer
 ties to the odd code, 21 quantizer shared exponent one octave high, 22
 quantizer keeps negative zero, 30 silu derivative missing a term, 31 W_down
 gradient written transposed, 32 router gradient without the softmax mean
-term."""
+term, 40 packed order: up rows taken from the gate half, 41 packed order:
+chunk base from the chunk's own width, 42 packed order: scale slots with
+(g, t) swapped."""
 import pytest
 
 import oracle
@@ -16,7 +18,7 @@ from tests import oracle_pins
 PLANTS = {1: "gate_up_swapped", 2: "tie_to_higher_index", 3: "down_transposed", 4: "unstable_permute",
           5: "nibble_order_swapped", 6: "silu_sign", 7: "weights_unnormalised", 20: "quant_ties_odd",
           21: "quant_exponent_high", 22: "quant_negative_zero", 30: "bwd_silu_grad", 31: "bwd_down_transposed",
-          32: "bwd_router_mean"}
+          32: "bwd_router_mean", 40: "pack_up_rows", 41: "pack_chunk_base", 42: "pack_scale_slots"}
 
 
 @pytest.mark.parametrize("plant", sorted(PLANTS), ids=lambda p: PLANTS[p])
