@@ -87,13 +87,13 @@ def measured_traffic(kernel: str):
 class Timed:
     """One workload on the device, with rotated weight copies."""
 
-    def __init__(self, layer, n_copies: int):
+    def __init__(self, layer, n_copies: int, packed: bool = False):
         import torch
 
         import mixture_experts_ffn_05_amd as moe
         from tests.gpu_layer import GpuLayer
         self.torch, self.moe = torch, moe
-        self.g = GpuLayer(layer)
+        self.g = GpuLayer(layer, packed=packed)
         c = layer.cfg
         g = self.g
         self.copies = [(g.gate_up, g.down, g.gate_up_scale, g.down_scale)]
@@ -206,15 +206,15 @@ def n_copies_for(cfg, touched_bytes):
     return max(4, min(16, int(4 * MALL_BYTES // max(touched_bytes, 1)) + 1))
 
 
-def bench_decode(layer, steps, warmup, graph=False):
+def bench_decode(layer, steps, warmup, graph=False, packed=False):
     import torch
-    probe = Timed(layer, 1)
+    probe = Timed(layer, 1, packed)
     probe.step(0)
     torch.cuda.synchronize()
     touched = probe.touched_experts()
     total_b, gu_b = layer_bytes(layer.cfg, touched)
     del probe
-    tm = Timed(layer, n_copies_for(layer.cfg, total_b))
+    tm = Timed(layer, n_copies_for(layer.cfg, total_b), packed)
     sec = tm.run(steps, warmup, graph)
     stages = tm.stages(steps)
     return tm, sec, stages, touched, total_b, gu_b
@@ -415,10 +415,12 @@ def bench_backward(steps: int, name: str = "20b_prefill_zipf"):
 HOST_LINK_GBS = 64.0  # PCIe Gen5 x16, one direction
 
 
-def bench_host_weights(name: str = "20b_mxfp4_decode", reps: int = 5):
+def bench_host_weights(name: str = "20b_mxfp4_decode", reps: int = 5, packed: bool = False):
     """Decode with the expert weights in pinned host memory (mapped; the skinny
     kernels read only the touched experts' rows over the host link): us per
-    layer and GB/s of touched weight bytes against the link's peak."""
+    layer and GB/s of touched weight bytes against the link's peak.  packed:
+    MXFP4 weights in the packed order (reordered on the device, then copied to
+    the host)."""
     import torch
 
     import mixture_experts_ffn_05_amd as moe
@@ -426,8 +428,11 @@ def bench_host_weights(name: str = "20b_mxfp4_decode", reps: int = 5):
     from tests.gpu_layer import GpuLayer
     from tests.host_weights import pinned_weights
     layer = synth.make_layer(name)
-    g = GpuLayer(layer)
-    parts = pinned_weights(layer.weights)
+    g = GpuLayer(layer, packed=packed)
+    w = layer.weights
+    if packed:
+        w = synth.Weights(1, *(t.cpu().numpy() for t in (g.gate_up, g.down, g.gate_up_scale, g.down_scale)))
+    parts = pinned_weights(w)
     if parts is None:
         return {"workload": name, "skipped": "pinned host memory not mapped"}
     ptrs = [p.dev for p in parts] + [None, None]
@@ -445,7 +450,8 @@ def bench_host_weights(name: str = "20b_mxfp4_decode", reps: int = 5):
     sec = e0.elapsed_time(e1) * 1e-3 / reps
     del g, parts
     torch.cuda.empty_cache()
-    return {"workload": name, "us_per_layer": round(sec * 1e6, 1), "touched_experts": touched,
+    return {"workload": name + (" (packed order)" if packed else ""), "us_per_layer": round(sec * 1e6, 1),
+            "touched_experts": touched,
             "gbs": round(total_b / sec / 1e9, 2), "link_peak_gbs": HOST_LINK_GBS,
             "link_frac": round(total_b / sec / 1e9 / HOST_LINK_GBS, 4), "gate_up_bytes": int(gu_b)}
 
@@ -478,9 +484,9 @@ def secondary(steps, graph=False):
     out = {}
     out["library_dense_gemm_bf16_tflops"] = library_gemm_tflops()
     # prefill regimes: MFMA-bound
-    for name in ("20b_prefill_zipf", "20b_mxfp4_prefill"):
-        layer = synth.make_layer(name)
-        tm = Timed(layer, 1)
+    for name in ("20b_prefill_zipf", "20b_mxfp4_prefill", "20b_mxfp4_prefill+packed"):
+        layer = synth.make_layer(name.split("+")[0])
+        tm = Timed(layer, 1, name.endswith("+packed"))
         sec = tm.run(max(3, steps // 10), 2)
         stages = tm.stages(max(3, steps // 10), 1)
         fl, fl_gu = layer_flops(layer.cfg)
@@ -492,12 +498,15 @@ def secondary(steps, graph=False):
                      "stages_us": {k: round(v, 1) for k, v in stages.items()}}
         del tm, layer
     # decode regimes: HBM-bound
-    layer = synth.make_layer("20b_mxfp4_decode")
-    tm, sec, stages, touched, total_b, gu_b = bench_decode(layer, steps, 10, graph)
-    out["20b_mxfp4_decode"] = {"tokens_per_s": round(layer.cfg.T / sec, 1), "us_per_layer": round(sec * 1e6, 1),
-                               "touched_experts": touched, "hbm_frac": round(total_b / sec / 1e9 / HBM_PEAK_GBS, 4),
-                               "stages_us": {k: round(v, 1) for k, v in stages.items()}}
-    del tm, layer
+    # MXFP4 decode in the row-major order and in the packed order (moe_mxfp4_pack)
+    for packed in (False, True):
+        layer = synth.make_layer("20b_mxfp4_decode")
+        tm, sec, stages, touched, total_b, gu_b = bench_decode(layer, steps, 10, graph, packed)
+        out["20b_mxfp4_decode" + ("+packed" if packed else "")] = {
+            "tokens_per_s": round(layer.cfg.T / sec, 1), "us_per_layer": round(sec * 1e6, 1),
+            "touched_experts": touched, "hbm_frac": round(total_b / sec / 1e9 / HBM_PEAK_GBS, 4),
+            "stages_us": {k: round(v, 1) for k, v in stages.items()}}
+        del tm, layer
     base = synth.CONFIGS["120b_sweep"]
     w120 = synth.make_weights(base)
     sweep = {}
@@ -513,6 +522,7 @@ def secondary(steps, graph=False):
     out["mxfp4_quantize_20b_gate_up"] = bench_quantize(steps)
     out["backward_20b_prefill_zipf"] = bench_backward(steps)
     out["host_weights_20b_mxfp4_decode"] = bench_host_weights("20b_mxfp4_decode")
+    out["host_weights_20b_mxfp4_decode+packed"] = bench_host_weights("20b_mxfp4_decode", packed=True)
     return out
 
 
@@ -560,9 +570,9 @@ def main():
             copy_probe()
         print(json.dumps(rec))
         return
-    if args.only:
-        layer = synth.make_layer(args.only)
-        tm = Timed(layer, 1)
+    if args.only:  # "<config>" or "<config>+packed" (MXFP4 weights in the packed order)
+        layer = synth.make_layer(args.only.split("+")[0])
+        tm = Timed(layer, 1, args.only.endswith("+packed"))
         sec = tm.run(args.steps, args.warmup)
         fl, _ = layer_flops(layer.cfg)
         print(json.dumps({"workload": args.only, "tokens": layer.cfg.T, "steps": args.steps,

@@ -45,6 +45,9 @@
  *            (OCP MX: E2M1 element 2b in the low nibble of byte b, element
  *             2b+1 in the high nibble; one E8M0 scale 2^(S-127) per 32
  *             consecutive elements along the input dimension)
+ *   gate_up, down  MXFP4 in the packed order (MOE_WFMT_MXFP4_PACKED): the same
+ *            bytes and scales, same array sizes, reordered by moe_mxfp4_pack
+ *            (the order is defined there)
  *   topk_idx       int32 [T][k]   slots in routing order
  *   topk_w         fp32  [T][k]
  *   expert_offsets int32 [E+1]    exclusive prefix sum of pairs per expert
@@ -63,7 +66,8 @@
  * section "llama-swap.yaml entry").
  *
  * Alignment: bf16 matrices, weight bytes and the workspace must be 16-byte
- * aligned; int32/fp32 arrays 4-byte aligned; scale arrays need no alignment.
+ * aligned; int32/fp32 arrays 4-byte aligned; row-major scale arrays need no
+ * alignment, packed-order scale arrays 8 bytes.
  * Supported sizes: 1 <= E <= 256, 1 <= k <= min(E, 8), H and I multiples of
  * 32, T >= 0 with T*k < 2^31.  T = 0 returns MOE_OK and launches nothing.
  *
@@ -103,7 +107,13 @@ enum {
     MOE_ERR_HIP = 5          /* a HIP launch failed; see moe_last_error() */
 };
 
-enum { MOE_WFMT_BF16 = 0, MOE_WFMT_MXFP4 = 1 };
+/* Expert weight formats.  MXFP4_PACKED holds MXFP4 weights in the packed
+ * order of moe_mxfp4_pack: every path accepts it, and the skinny (decode)
+ * regime streams it as long contiguous runs.  Its skinny kernel addresses
+ * with 32-bit offsets: it needs I*H < 2^31, T*H < 2^30 and T*k*I < 2^30.
+ * Outside those sizes MOE_PATH_SKINNY returns MOE_ERR_UNSUPPORTED and
+ * MOE_PATH_AUTO takes the tiled path. */
+enum { MOE_WFMT_BF16 = 0, MOE_WFMT_MXFP4 = 1, MOE_WFMT_MXFP4_PACKED = 2 };
 
 /* Expert-FFN schedule.  AUTO picks SKINNY when tokens per expert are few
  * (weight streaming at HBM rate) and TILED otherwise (LDS-tiled grouped GEMM).
@@ -226,6 +236,36 @@ int moe_mxfp4_quantize(int64_t rows, int32_t cols, const void* w, uint8_t* packe
  * a bf16 value, so out is exact.  Same arguments rules as moe_mxfp4_quantize;
  * out must be 16-byte aligned and must not overlap w. */
 int moe_mxfp4_fakequant(int64_t rows, int32_t cols, const void* w, void* out, void* stream);
+
+/* Packed MXFP4 order: reorders one MXFP4 expert tensor (bytes and scales) for
+ * weight streaming in the decode regime.  This is the library's own storage
+ * order, not the pages': they fix the MXFP4 format ("Persona Kappa: training
+ * a 20B LLM on desktop GPUs", section "Quantization-Aware Training (QAT)"),
+ * and the packed order changes no byte or scale value, it only moves them.
+ * It is a one-time step at weight load; the layer then runs with
+ * dims->wfmt = MOE_WFMT_MXFP4_PACKED.
+ *
+ * which = MOE_PACK_GATE_UP: w [E][2I][H/2], scales [E][2I][H/32] (K = H);
+ * which = MOE_PACK_DOWN:    w [E][H][I/2],  scales [E][H][I/32]  (K = I).
+ * Per expert a piece is the 16 bytes of one row over K-block kb (elements
+ * 32kb..32kb+31) and it carries that block's scale.  Rows form items of 32
+ * slots: a gate/up item i holds gate rows 16i..16i+15 (slots 0-15) and the
+ * matching up rows I+16i..I+16i+15 (slots 16-31); a down item i holds rows
+ * 32i..32i+31.  With slot q = 4g + t (g < 8, t < 4), kb = 16c + b (b < 16),
+ * nkb = K/32 and nb(c) = min(16, nkb - 16c), the piece of (item i, slot q,
+ * kb) goes to byte i*512*nkb + c*8192 + g*64*nb(c) + 16*(4b + t) of the
+ * expert's packed bytes and its scale to byte i*32*nkb + c*512 + 8*(4b + t)
+ * + g of the expert's packed scales; experts keep the row-major strides.
+ * Outputs w_packed [same size as w], scales_packed [same size as scales].
+ * Uses dims->E, H, I (validated as for the layer; T, k, path are checked
+ * but unused).  Errors: dims invalid -> as moe_forward; which not one of
+ * MOE_PACK_* or a null pointer -> MOE_ERR_INVALID_ARG; w or w_packed not
+ * 16-byte aligned or scales_packed not 8-byte aligned -> MOE_ERR_MISALIGNED;
+ * an output overlapping an input or the other output -> MOE_ERR_INVALID_ARG.
+ * Asynchronous on `stream` like every call. */
+enum { MOE_PACK_GATE_UP = 0, MOE_PACK_DOWN = 1 };
+int moe_mxfp4_pack(const moe_dims* dims, int32_t which, const uint8_t* w, const uint8_t* scales, uint8_t* w_packed,
+                   uint8_t* scales_packed, void* stream);
 
 /* Static text for an error code. */
 const char* moe_strerror(int code);

@@ -18,12 +18,13 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_MISALIGNED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(6)
-MOE_WFMT_BF16, MOE_WFMT_MXFP4 = 0, 1
+MOE_WFMT_BF16, MOE_WFMT_MXFP4, MOE_WFMT_MXFP4_PACKED = 0, 1, 2
+MOE_PACK_GATE_UP, MOE_PACK_DOWN = 0, 1
 MOE_PATH_AUTO, MOE_PATH_SKINNY, MOE_PATH_TILED = 0, 1, 2
 
 EXPORTED = ("moe_workspace_size", "moe_route", "moe_permute", "moe_gate_up", "moe_down", "moe_grouped_ffn",
-            "moe_combine", "moe_forward", "moe_backward_workspace_size", "moe_backward", "moe_mxfp4_quantize", "moe_mxfp4_fakequant", "moe_strerror",
-            "moe_last_error")
+            "moe_combine", "moe_forward", "moe_backward_workspace_size", "moe_backward", "moe_mxfp4_quantize",
+            "moe_mxfp4_fakequant", "moe_mxfp4_pack", "moe_strerror", "moe_last_error")
 
 
 class MoeLibraryMissing(RuntimeError):
@@ -76,6 +77,7 @@ def library(path: str | None = None):
         "moe_backward": [D, V, V, W, V, V, V, V, V, V, SZ, V],
         "moe_mxfp4_quantize": [ctypes.c_int64, ctypes.c_int32, V, V, V, V],
         "moe_mxfp4_fakequant": [ctypes.c_int64, ctypes.c_int32, V, V, V],
+        "moe_mxfp4_pack": [D, ctypes.c_int32, V, V, V, V, V],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -195,8 +197,13 @@ def moe_mxfp4_fakequant(rows: int, cols: int, w, out, stream=None):
     _check("moe_mxfp4_fakequant", library().moe_mxfp4_fakequant(rows, cols, _ptr(w), _ptr(out), _stream(stream)))
 
 
+def moe_mxfp4_pack(d: moe_dims, which: int, w, scales, w_packed, scales_packed, stream=None):
+    _check("moe_mxfp4_pack", library().moe_mxfp4_pack(ctypes.byref(d), which, _ptr(w), _ptr(scales), _ptr(w_packed),
+                                                     _ptr(scales_packed), _stream(stream)))
+
+
 __all__ = ["library", "dims", "expert_weights", "strerror", "moe_workspace_size", "moe_route", "moe_permute",
            "moe_gate_up", "moe_down", "moe_grouped_ffn", "moe_combine", "moe_forward", "moe_backward_workspace_size",
            "moe_backward", "moe_mxfp4_quantize",
-           "moe_mxfp4_fakequant", "moe_dims",
+           "moe_mxfp4_fakequant", "moe_mxfp4_pack", "moe_dims",
            "moe_expert_weights", "MoeError", "MoeLibraryMissing", "EXPORTED", "LIB_PATH"]

@@ -367,13 +367,401 @@ static hipError_t launch_skinny(const FfnArgs& a, hipStream_t s)
     return hipGetLastError();
 }
 
+
+// ---------------------------------------------------------------------------
+// MXFP4 skinny kernel on v_mfma_f32_4x4x4_16b_bf16.  That instruction runs 16
+// independent 4x4x4 products per wave: lane (block b, t) supplies row t of
+// the block's A and column t of its B, each with 4 consecutive K values, and
+// receives column t of the block's 4x4 result.  Here every block owns its own
+// K range, so a block multiplies 4 weight rows by 4 tokens over K-block b
+// (32 K) of each 512-K chunk, and only the real tokens' activations are
+// loaded: lane (b, t) loads token t's 32 bf16 at that K-block (64 B), where a
+// 16x16 MFMA would move 16 token columns whatever the count.  A wave item is
+// 32 weight rows (8 groups of 4; gate/up: 16 gate rows then the 16 matching
+// up rows) and 4 or 8 tokens per pass (TG groups of 4).  Per chunk lane
+// (b, t) loads, from HBM straight into registers, the 16 bytes of E2M1 codes
+// of row 4g+t at its K-block for each group g with the 8 scale bytes, and
+// token 4*tg+t's activations; the E2M1 codes are decoded once and used by the
+// TG token groups.  No LDS and no barrier: waves are independent.  After the
+// last chunk of a pass the 16 blocks' partial sums are added across lanes.
+//
+// Weights in the packed MXFP4 order (documented with moe_mxfp4_pack) make each
+// group's 16-byte pieces 1 KB of consecutive bytes per wave load and put a
+// lane's 8 scale bytes in one 8-byte word; in the row-major order a load
+// covers 4 rows x 256 B and the scales take 8 byte loads per chunk.
+constexpr int S4_RG = 8;                 // 4-row groups per item (32 rows)
+constexpr int S4_KB = 16;                // K-blocks per chunk, one per MFMA block
+constexpr int S4_KC = S4_KB * 32;        // K per chunk
+constexpr int S4_THREADS = 256;
+constexpr int S4_WPB = S4_THREADS / WAVE;
+constexpr uint32_t S4_OOB = 0x80000000u; // buffer offset past every range: loads return zero
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+
+struct S4Cursor {
+    int item;  // -1: past the end
+    int e, it, s0, M, j0, kc;  // expert, item inside the expert, segment, token pass, K chunk
+};
+
+template <bool PACKED, int TG>
+struct S4Buf {
+    u32x4 w[S4_RG];                   // E2M1 codes of row 4g+t at this lane's K-block
+    uint32_t s[PACKED ? 2 : S4_RG];   // scale bytes: packed 8 per two words, else one per word
+    u32x4 x[TG][4];                   // token 4*tg+t: 32 bf16 at this lane's K-block
+};
+
+__device__ __forceinline__ f32x4 mfma4(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, f32x4 c)
+{
+    const s16x4 a = __builtin_bit_cast(s16x4, uint2{a0, a1});
+    const s16x4 b = __builtin_bit_cast(s16x4, uint2{b0, b1});
+    return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(a, b, c, 0, 0, 0);
+}
+
+// The layer's expert segments, read once per wave: bit l of mask[j] says
+// expert 64j + l has tokens; this lane holds offsets[64j + lane] and
+// offsets[64j + lane + 1].  Items are decoded from it without memory access,
+// so a wave moving to its next item never waits on its loads in flight.
+struct S4Experts {
+    uint64_t mask[4];
+    int lo[4], hi[4];
+    int active;  // experts with tokens
+};
+
+__device__ __forceinline__ S4Experts s4_experts(const FfnArgs& a)
+{
+    S4Experts x;
+    x.active = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {  // E <= 256
+        const int e = 64 * j + lane_id();
+        x.lo[j] = e < a.E ? a.offsets[e] : 0;
+        x.hi[j] = e < a.E ? a.offsets[e + 1] : 0;
+        x.mask[j] = ballot(x.hi[j] > x.lo[j]);
+        x.active += __popcll(x.mask[j]);
+    }
+    return x;
+}
+
+__device__ __forceinline__ S4Cursor s4_item(const S4Experts& x, int item, int n_items, int tiles)
+{
+    S4Cursor c;
+    c.item = item < n_items ? item : -1;
+    c.j0 = c.kc = 0;
+    c.e = c.it = c.s0 = c.M = 0;
+    if (c.item >= 0) {
+        int r = item / tiles;  // rank of the expert among those with tokens
+        c.it = item % tiles;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int cnt = __popcll(x.mask[j]);
+            if (r >= 0 && r < cnt) {
+                const uint32_t lo = (uint32_t)x.mask[j], hi = (uint32_t)(x.mask[j] >> 32);
+                const int before = __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0u));
+                const uint64_t hit = ballot(((x.mask[j] >> lane_id()) & 1) && before == r);
+                const int l = (int)__builtin_ctzll(hit);
+                c.e = 64 * j + l;
+                c.s0 = __builtin_amdgcn_readlane(x.lo[j], l);
+                c.M = __builtin_amdgcn_readlane(x.hi[j], l) - c.s0;
+            }
+            r -= cnt;
+        }
+    }
+    return c;
+}
+
+template <int TG>
+__device__ __forceinline__ S4Cursor s4_next(const S4Experts& x, const S4Cursor& c, int K, int n_items, int tiles,
+                                            int nw)
+{
+    S4Cursor n = c;
+    if (c.item < 0) return n;
+    n.kc += S4_KC;
+    if (n.kc < K) return n;
+    n.kc = 0;
+    n.j0 += 4 * TG;
+    if (n.j0 < n.M) return n;
+    return s4_item(x, c.item + nw, n_items, tiles);
+}
+
+// Row (inside the expert) that lane t supplies for group g of item it.
+template <bool GATE_UP>
+__device__ __forceinline__ int s4_row(const FfnArgs& a, int it, int g, int t)
+{
+    if constexpr (GATE_UP)  // groups 0-3: gate columns 16it..; groups 4-7: the matching up rows
+        return g < 4 ? 16 * it + 4 * g + t : a.I + 16 * it + 4 * (g - 4) + t;
+    else
+        return 32 * it + 4 * g + t;
+}
+
+// Pair indices of this lane's tokens in cursor c's pass (gate/up only), as
+// buffer loads so that they are in flight one step ahead of their use.
+template <int TG>
+__device__ __forceinline__ void s4_pairs(const FfnArgs& a, const S4Cursor& c, uint32_t (&p)[TG])
+{
+    const int t = lane_id() & 3;
+    const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int32_t*>(a.sorted_pairs), (short)0, a.T * a.k * 4, 0x00020000);
+#pragma unroll
+    for (int tg = 0; tg < TG; ++tg) {
+        const int j = c.j0 + 4 * tg + t;
+        const bool ok = c.item >= 0 && j < c.M;
+        p[tg] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(pr, ok ? (uint32_t)(c.s0 + j) * 4u : S4_OOB, 0, 0);
+    }
+}
+
+// Byte offset of the activation row of this lane's token in group tg of
+// cursor c's pass, or S4_OOB when there is no such token.
+template <bool GATE_UP>
+__device__ __forceinline__ uint32_t s4_xrow(const FfnArgs& a, const S4Cursor& c, int tg, uint32_t pair)
+{
+    const int j = c.j0 + 4 * tg + (lane_id() & 3);
+    const bool ok = c.item >= 0 && j < c.M;
+    uint32_t row;
+    if constexpr (GATE_UP)
+        row = (pair / (uint32_t)a.k) * (uint32_t)a.H * 2u;
+    else
+        row = (uint32_t)(c.s0 + j) * (uint32_t)a.I * 2u;
+    return ok ? row : S4_OOB;
+}
+
+// Issue chunk c's loads into b.  Past-the-end cursors and K-blocks past the
+// row read zeros through the buffer range checks, so every step issues the
+// same loads with no branch.
+template <bool PACKED, int TG, bool GATE_UP>
+__device__ __forceinline__ void s4_fetch(const FfnArgs& a, const S4Cursor& c, const uint32_t (&xrow)[TG], int K,
+                                         S4Buf<PACKED, TG>& b)
+{
+    const int lane = lane_id(), blk = lane >> 2, t = lane & 3;
+    const int R = GATE_UP ? 2 * a.I : a.H;  // weight rows per expert
+    const int nkb = K / 32;
+    const bool live = c.item >= 0;
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(static_cast<const uint8_t*>(a.w) + (size_t)c.e * R * (K / 2)), (short)0,
+        live ? R * (K / 2) : 0, 0x00020000);
+    const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(a.w_scale + (size_t)c.e * R * nkb), (short)0, live ? R * nkb : 0, 0x00020000);
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(GATE_UP ? a.x : a.a_rows), (short)0,
+        GATE_UP ? a.T * a.H * 2 : a.T * a.k * a.I * 2, 0x00020000);
+    const int kb = c.kc / 32 + blk;  // this lane's K-block
+    const bool kin = kb < nkb;
+    if constexpr (PACKED) {
+        const int cc = c.kc / S4_KC, nb = min(S4_KB, nkb - S4_KB * cc);
+        const uint32_t wb = (uint32_t)c.it * 512u * nkb + (uint32_t)cc * 8192u + 16u * lane;
+#pragma unroll
+        for (int g = 0; g < S4_RG; ++g)
+            b.w[g] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                   wr, kin ? wb + (uint32_t)(64 * nb * g) : S4_OOB, 0, 2));
+        const uint32_t sb = (uint32_t)c.it * 32u * nkb + (uint32_t)cc * 512u + 8u * lane;
+        const uint2 sv = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(sr, kin ? sb : S4_OOB, 0, 2));
+        b.s[0] = sv.x;
+        b.s[1] = sv.y;
+    } else {
+#pragma unroll
+        for (int g = 0; g < S4_RG; ++g) {
+            const uint32_t row = (uint32_t)s4_row<GATE_UP>(a, c.it, g, t);
+            b.w[g] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                   wr, kin ? row * (uint32_t)(K / 2) + 16u * kb : S4_OOB, 0, 2));
+        }
+#pragma unroll
+        for (int g = 0; g < S4_RG; ++g) {
+            const uint32_t row = (uint32_t)s4_row<GATE_UP>(a, c.it, g, t);
+            b.s[g] = __builtin_amdgcn_raw_buffer_load_b8(sr, kin ? row * (uint32_t)nkb + kb : S4_OOB, 0, 2);
+        }
+    }
+#pragma unroll
+    for (int tg = 0; tg < TG; ++tg) {
+        const uint32_t xo = kin ? xrow[tg] + 64u * kb : S4_OOB;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            b.x[tg][q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, xo + 16u * q, 0, 0));
+    }
+}
+
+// Byte SEL of q (two E2M1 codes, low nibble first) times scale, as two bf16.
+template <int SEL>
+__device__ __forceinline__ uint32_t cvt_fp4_pair(uint32_t q, float scale)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, scale, SEL));
+}
+
+template <bool PACKED, int TG>
+__device__ __forceinline__ void s4_compute(const S4Buf<PACKED, TG>& b, f32x4 (&acc)[TG][S4_RG])
+{
+    float sc[S4_RG];
+#pragma unroll
+    for (int g = 0; g < S4_RG; ++g)
+        sc[g] = e8m0_to_f32(PACKED ? (b.s[g / 4] >> (8 * (g % 4))) & 0xFFu : b.s[g]);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {  // 4 K per step: codes 4s..4s+3 = bytes 2s, 2s+1 of the lane's 16
+        uint32_t x0[TG], x1[TG];
+#pragma unroll
+        for (int tg = 0; tg < TG; ++tg) {
+            const u32x4 xv = b.x[tg][s / 2];
+            x0[tg] = (s & 1) ? xv.z : xv.x;
+            x1[tg] = (s & 1) ? xv.w : xv.y;
+        }
+#pragma unroll
+        for (int g = 0; g < S4_RG; ++g) {
+            const uint32_t q = b.w[g][s / 2];
+            const uint32_t a0 = (s & 1) ? cvt_fp4_pair<2>(q, sc[g]) : cvt_fp4_pair<0>(q, sc[g]);
+            const uint32_t a1 = (s & 1) ? cvt_fp4_pair<3>(q, sc[g]) : cvt_fp4_pair<1>(q, sc[g]);
+#pragma unroll
+            for (int tg = 0; tg < TG; ++tg) acc[tg][g] = mfma4(a0, a1, x0[tg], x1[tg], acc[tg][g]);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // decode one K step at a time (hoisting them all spills)
+    }
+}
+
+// One step of the cross-block sum: keep v[0 .. 16>>J) (the half selected by
+// bit J of this lane's block) and add the partner block's copies of it.
+template <int J>
+__device__ __forceinline__ void s4_halve(float (&v)[32], int blk)
+{
+    constexpr int half = 16 >> J;
+    const bool hi = (blk >> J) & 1;
+#pragma unroll
+    for (int ci = 0; ci < half; ++ci) {
+        const float send = hi ? v[ci] : v[ci + half];
+        const float keep = hi ? v[ci + half] : v[ci];
+        v[ci] = keep + __shfl_xor(send, 4 << J, WAVE);
+    }
+}
+
+// Sum the 16 blocks' partials of token group tg and write its outputs.  v[ci]
+// stands for item row i(ci); every step keeps half of the values and adds the
+// partner lane's copies, so after 4 steps lane (b, t) holds two rows summed
+// over all blocks: gate/up: gate row n and up row n with n = bitrev4(b);
+// down: rows 2*bitrev4(b) and 2*bitrev4(b)+1.
+template <bool GATE_UP>
+__device__ __forceinline__ void s4_epilogue(const FfnArgs& a, const S4Cursor& c, int tg, f32x4 (&acc)[S4_RG])
+{
+    const int lane = lane_id(), blk = lane >> 2, t = lane & 3;
+    float v[32];
+#pragma unroll
+    for (int ci = 0; ci < 32; ++ci) {
+        // index bits from low: gate/up [row bit 4, row bits 0..3]; down [row bits 0..4]
+        const int i = GATE_UP ? (((ci >> 1) & 15) | ((ci & 1) << 4)) : ci;
+        v[ci] = acc[i / 4][i % 4];
+    }
+    s4_halve<0>(v, blk);
+    s4_halve<1>(v, blk);
+    s4_halve<2>(v, blk);
+    s4_halve<3>(v, blk);
+    const int rb = ((blk & 1) << 3) | ((blk & 2) << 1) | ((blk & 4) >> 1) | ((blk & 8) >> 3);  // bitrev4(blk)
+    const int j = c.j0 + 4 * tg + t;
+    if (j < c.M) {
+        if constexpr (GATE_UP) {
+            a.out[(size_t)(c.s0 + j) * a.I + 16 * c.it + rb] = (uint16_t)f32_to_bf16(silu(v[0]) * v[1]);
+        } else {
+            *reinterpret_cast<uint32_t*>(a.out + (size_t)(c.s0 + j) * a.H + 32 * c.it + 2 * rb) =
+                pack_bf16x2(v[0], v[1]);
+        }
+    }
+#pragma unroll
+    for (int g = 0; g < S4_RG; ++g) acc[g] = f32x4{0, 0, 0, 0};
+}
+
+// One pipeline step: fetch cursor c1's chunk into nxt while multiplying c0's
+// (in cur), and finish c0's pass if c1 starts another.  p holds c1's pair
+// indices (loaded one step ago) and receives c2's.
+template <bool PACKED, int TG, bool GATE_UP>
+__device__ __forceinline__ void s4_step(const FfnArgs& a, const S4Experts& x, int K, int n_items, int tiles, int nw,
+                                        S4Cursor& c0, S4Cursor& c1, uint32_t (&p)[TG], S4Buf<PACKED, TG>& cur,
+                                        S4Buf<PACKED, TG>& nxt, f32x4 (&acc)[TG][S4_RG])
+{
+    uint32_t xrow[TG];
+#pragma unroll
+    for (int tg = 0; tg < TG; ++tg) xrow[tg] = s4_xrow<GATE_UP>(a, c1, tg, p[tg]);
+    const S4Cursor c2 = s4_next<TG>(x, c1, K, n_items, tiles, nw);
+    if constexpr (GATE_UP) s4_pairs<TG>(a, c2, p);
+    s4_fetch<PACKED, TG, GATE_UP>(a, c1, xrow, K, nxt);
+    s4_compute<PACKED, TG>(cur, acc);
+    if (c1.item != c0.item || c1.j0 != c0.j0) {
+        mfma_drain();
+#pragma unroll
+        for (int tg = 0; tg < TG; ++tg) s4_epilogue<GATE_UP>(a, c0, tg, acc[tg]);
+    }
+    c0 = c1;
+    c1 = c2;
+}
+
+// Persistent over items: wave w takes items w, w + nw, ... (item = touched
+// expert x 32-row tile; gate/up N = I, K = H; down N = H, K = I).
+template <bool PACKED, int TG, bool GATE_UP>
+__global__ __launch_bounds__(S4_THREADS, 2) void skinny4_kernel(FfnArgs a)
+{
+    const int K = GATE_UP ? a.H : a.I;
+    const int tiles = GATE_UP ? a.I / 16 : a.H / 32;
+    const S4Experts x = s4_experts(a);
+    const int n_items = x.active * tiles;
+    const int nw = gridDim.x * S4_WPB;
+    const int w = blockIdx.x * S4_WPB + __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);  // uniform per wave
+    S4Cursor c0 = s4_item(x, w, n_items, tiles);
+    if (c0.item < 0) return;  // uniform per wave
+
+    S4Buf<PACKED, TG> b0, b1;
+    uint32_t p[TG], xrow[TG];
+#pragma unroll
+    for (int tg = 0; tg < TG; ++tg) p[tg] = 0u;
+    if constexpr (GATE_UP) s4_pairs<TG>(a, c0, p);
+#pragma unroll
+    for (int tg = 0; tg < TG; ++tg) xrow[tg] = s4_xrow<GATE_UP>(a, c0, tg, p[tg]);
+    s4_fetch<PACKED, TG, GATE_UP>(a, c0, xrow, K, b0);
+    S4Cursor c1 = s4_next<TG>(x, c0, K, n_items, tiles, nw);
+    if constexpr (GATE_UP) s4_pairs<TG>(a, c1, p);
+    f32x4 acc[TG][S4_RG];
+#pragma unroll
+    for (int tg = 0; tg < TG; ++tg)
+#pragma unroll
+        for (int g = 0; g < S4_RG; ++g) acc[tg][g] = f32x4{0, 0, 0, 0};
+    while (true) {  // two steps per iteration so the buffers swap roles without copies
+        s4_step<PACKED, TG, GATE_UP>(a, x, K, n_items, tiles, nw, c0, c1, p, b0, b1, acc);
+        if (c0.item < 0) break;
+        s4_step<PACKED, TG, GATE_UP>(a, x, K, n_items, tiles, nw, c0, c1, p, b1, b0, acc);
+        if (c0.item < 0) break;
+    }
+}
+
+bool skinny4_supported(const FfnArgs& a)
+{
+    // 32-bit buffer offsets: one expert's weights, the activations and the
+    // pair list must each stay below 2^31 bytes
+    const long long lim = 1ll << 31;
+    const long long P = (long long)a.T * a.k;
+    return (long long)a.I * a.H < lim && (long long)a.T * a.H * 2 < lim && P * a.I * 2 < lim && P * 4 < lim;
+}
+
+template <bool PACKED, int TG, bool GATE_UP>
+static hipError_t launch_skinny4_tg(const FfnArgs& a, hipStream_t s)
+{
+    static const int cap =
+        resident_blocks(reinterpret_cast<const void*>(&skinny4_kernel<PACKED, TG, GATE_UP>), S4_THREADS);
+    const int P = a.T * a.k;
+    const int tiles = GATE_UP ? a.I / 16 : a.H / 32;
+    const long long waves = (long long)(P < a.E ? P : a.E) * tiles;
+    const long long blocks = (waves + S4_WPB - 1) / S4_WPB;
+    const int grid = (int)(blocks < cap ? blocks : cap);
+    hipLaunchKernelGGL((skinny4_kernel<PACKED, TG, GATE_UP>), dim3(grid), dim3(S4_THREADS), 0, s, a);
+    return hipGetLastError();
+}
+
+// An expert sees at most T tokens: one 4-token group covers T <= 4, else two
+// groups (8 tokens per pass over the weights).
+template <bool PACKED, bool GATE_UP>
+static hipError_t launch_skinny4(const FfnArgs& a, hipStream_t s)
+{
+    return a.T <= 4 ? launch_skinny4_tg<PACKED, 1, GATE_UP>(a, s) : launch_skinny4_tg<PACKED, 2, GATE_UP>(a, s);
+}
+
 hipError_t launch_gate_up_skinny(const FfnArgs& a, hipStream_t s)
 {
+    if (a.wfmt == 2) return launch_skinny4<true, true>(a, s);
     return a.wfmt == 0 ? launch_skinny<0, true>(a, s) : launch_skinny<1, true>(a, s);
 }
 
 hipError_t launch_down_skinny(const FfnArgs& a, hipStream_t s)
 {
+    if (a.wfmt == 2) return launch_skinny4<true, false>(a, s);
     return a.wfmt == 0 ? launch_skinny<0, false>(a, s) : launch_skinny<1, false>(a, s);
 }
 

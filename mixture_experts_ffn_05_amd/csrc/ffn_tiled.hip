@@ -266,9 +266,31 @@ __global__ __launch_bounds__(GM_THREADS, GM_WAVES / 4) void gemm_kernel(FfnArgs 
     // width read the tile's first row (never stored).
     const int nstages = K / GM_BK;
     long long qrow = 0;
-    if constexpr (WFMT == 1) {
+    if constexpr (WFMT != 0) {
         qrow = gm_wrow<GATE_UP>(a, e, n0, NOUT, tid >> 1);
         if (qrow < 0) qrow = gm_wrow<GATE_UP>(a, e, 0, NOUT, 0);
+    }
+    // Packed MXFP4 order (moe_mxfp4_pack): the row's 16-byte piece of K-block
+    // kb = 16c + b and its scale sit at pbase + c*8192 + g*64*nb(c) + 64b and
+    // psbase + c*512 + 32b, with slot 4g+t of item `it` fixed per thread.
+    long long pbase = 0, psbase = 0;
+    int pg = 0;
+    if constexpr (WFMT == 2) {
+        const int R = GATE_UP ? 2 * a.I : a.H, nkb = K / 32;
+        const long long eq = qrow / R;
+        const int r = (int)(qrow % R);
+        int it, q;
+        if constexpr (GATE_UP) {
+            const int n = r < a.I ? r : r - a.I;
+            it = n / 16;
+            q = n % 16 + (r < a.I ? 0 : 16);
+        } else {
+            it = r / 32;
+            q = r % 32;
+        }
+        pg = q / 4;
+        pbase = eq * R * (K / 2) + (long long)it * 512 * nkb + 16 * (q % 4);
+        psbase = eq * R * nkb + (long long)it * 32 * nkb + 8 * (q % 4) + pg;
     }
     const int qh = tid & 1;
     uint2 qw[2];
@@ -278,8 +300,16 @@ __global__ __launch_bounds__(GM_THREADS, GM_WAVES / 4) void gemm_kernel(FfnArgs 
     // of loads and the loop body has no branches.
     auto fetch_q = [&](int set, int st) {
         const int kk = min(st, nstages - 1) * GM_BK;
-        qw[set] = *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(a.w) + qrow * (K / 2) + kk / 2 + 8 * qh);
-        qsc[set] = a.w_scale[qrow * (K / 32) + kk / 32];
+        if constexpr (WFMT == 2) {
+            const int kb = kk / 32, c = kb >> 4, b = kb & 15, nb = min(16, K / 32 - 16 * c);
+            const long long off = pbase + 8192ll * c + 64 * pg * nb + 64 * b;
+            qw[set] = *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(a.w) + off + 8 * qh);
+            qsc[set] = a.w_scale[psbase + 512ll * c + 32 * b];
+        } else {
+            qw[set] = *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(a.w) + qrow * (K / 2) + kk / 2 +
+                                                      8 * qh);
+            qsc[set] = a.w_scale[qrow * (K / 32) + kk / 32];
+        }
     };
     auto store_q = [&](int set, int buf) {
         const float sc = e8m0_to_f32(qsc[set]);
@@ -289,7 +319,7 @@ __global__ __launch_bounds__(GM_THREADS, GM_WAVES / 4) void gemm_kernel(FfnArgs 
     // Vector-memory operations per wave per stage (vmcnt bookkeeping): direct
     // loads, and the MXFP4 register loads.
     constexpr int L = (WFMT == 0 ? 2 : 1) * GM_DL;
-    constexpr int QL = WFMT == 1 ? 2 : 0;
+    constexpr int QL = WFMT != 0 ? 2 : 0;
     // Issue the direct loads of stage st into buffer st % NBUF.
     auto issue = [&](int st) {
         const int buf = st % GM_NBUF, kk = min(st, nstages - 1) * GM_BK;
@@ -344,7 +374,7 @@ __global__ __launch_bounds__(GM_THREADS, GM_WAVES / 4) void gemm_kernel(FfnArgs 
     // (an expert without tokens in the weight-gradient mode has no K: its tile is zero)
     if (!WGRAD || nstages > 0) {
     for (int st = 0; st < GM_DIST; ++st) issue(st);
-    if constexpr (WFMT == 1) {
+    if constexpr (WFMT != 0) {
         fetch_q(0, 0);
         fetch_q(1, 1);
         store_q(0, 0);
@@ -365,7 +395,7 @@ __global__ __launch_bounds__(GM_THREADS, GM_WAVES / 4) void gemm_kernel(FfnArgs 
         mma(f0);
         interleave();
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (WFMT == 1) {
+        if constexpr (WFMT != 0) {
             store_q(SET, nb);             // stage st+1, fetched two stages ago
             fetch_q(SET, st + 3);
         }
@@ -476,12 +506,16 @@ static hipError_t launch_gemm(const FfnArgs& a, hipStream_t s)
 
 hipError_t launch_gate_up_tiled(const FfnArgs& a, hipStream_t s)
 {
-    return a.wfmt == 0 ? launch_gemm<0, true>(a, s) : launch_gemm<1, true>(a, s);
+    return a.wfmt == 0   ? launch_gemm<0, true>(a, s)
+           : a.wfmt == 1 ? launch_gemm<1, true>(a, s)
+                         : launch_gemm<2, true>(a, s);
 }
 
 hipError_t launch_down_tiled(const FfnArgs& a, hipStream_t s)
 {
-    return a.wfmt == 0 ? launch_gemm<0, false>(a, s) : launch_gemm<1, false>(a, s);
+    return a.wfmt == 0   ? launch_gemm<0, false>(a, s)
+           : a.wfmt == 1 ? launch_gemm<1, false>(a, s)
+                         : launch_gemm<2, false>(a, s);
 }
 
 hipError_t launch_wgrad_tiled(const uint16_t* A, const uint16_t* B, const int32_t* padoff, int E, int M, int N,

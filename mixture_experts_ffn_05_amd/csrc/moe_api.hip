@@ -46,6 +46,19 @@ Layout layout_for(const moe_dims& d)
     return L;
 }
 
+// Sizes within the 32-bit buffer offsets of the packed-order skinny kernel.
+bool packed_skinny_fits(const moe_dims& d)
+{
+    moe::FfnArgs a;
+    memset(&a, 0, sizeof a);
+    a.T = d.T;
+    a.H = d.H;
+    a.E = d.E;
+    a.k = d.k;
+    a.I = d.I;
+    return moe::skinny4_supported(a);
+}
+
 int check_dims(const moe_dims* d)
 {
     if (!d) return MOE_ERR_INVALID_ARG;
@@ -53,8 +66,11 @@ int check_dims(const moe_dims* d)
     if ((int64_t)d->T * d->k > INT32_MAX) return MOE_ERR_INVALID_ARG;
     if (d->E > 256 || d->k > 8) return MOE_ERR_UNSUPPORTED;
     if (d->H % 32 != 0 || d->I % 32 != 0) return MOE_ERR_UNSUPPORTED;
-    if (d->wfmt != MOE_WFMT_BF16 && d->wfmt != MOE_WFMT_MXFP4) return MOE_ERR_UNSUPPORTED;
+    if (d->wfmt != MOE_WFMT_BF16 && d->wfmt != MOE_WFMT_MXFP4 && d->wfmt != MOE_WFMT_MXFP4_PACKED)
+        return MOE_ERR_UNSUPPORTED;
     if (d->path != MOE_PATH_AUTO && d->path != MOE_PATH_SKINNY && d->path != MOE_PATH_TILED)
+        return MOE_ERR_UNSUPPORTED;
+    if (d->wfmt == MOE_WFMT_MXFP4_PACKED && d->path == MOE_PATH_SKINNY && !packed_skinny_fits(*d))
         return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
@@ -73,7 +89,9 @@ int check_weights(const moe_dims& d, const moe_expert_weights* w)
     if (!w) return MOE_ERR_INVALID_ARG;
     int rc;
     if ((rc = check_ptr(w->gate_up, 16)) || (rc = check_ptr(w->down, 16))) return rc;
-    if (d.wfmt == MOE_WFMT_MXFP4 && (!w->gate_up_scale || !w->down_scale)) return MOE_ERR_INVALID_ARG;
+    if (d.wfmt != MOE_WFMT_BF16 && (!w->gate_up_scale || !w->down_scale)) return MOE_ERR_INVALID_ARG;
+    if (d.wfmt == MOE_WFMT_MXFP4_PACKED && (!aligned(w->gate_up_scale, 8) || !aligned(w->down_scale, 8)))
+        return MOE_ERR_MISALIGNED;
     return MOE_OK;
 }
 
@@ -105,7 +123,7 @@ bool use_skinny(const moe_dims& d)
 {
     if (d.path == MOE_PATH_SKINNY) return true;
     if (d.path == MOE_PATH_TILED) return false;
-    return d.T <= kSkinnyMaxT;
+    return d.T <= kSkinnyMaxT && (d.wfmt != MOE_WFMT_MXFP4_PACKED || packed_skinny_fits(d));
 }
 
 moe::FfnArgs ffn_args(const moe_dims& d)
@@ -486,6 +504,29 @@ int moe_mxfp4_quantize(int64_t rows, int32_t cols, const void* w, uint8_t* packe
     if (!scales) return MOE_ERR_INVALID_ARG;
     return hip_status(moe::launch_mxfp4_quantize(static_cast<const uint16_t*>(w), n, packed, scales,
                                                  static_cast<hipStream_t>(stream)));
+}
+
+int moe_mxfp4_pack(const moe_dims* dims, int32_t which, const uint8_t* w, const uint8_t* scales, uint8_t* w_packed,
+                   uint8_t* scales_packed, void* stream)
+{
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    if (which != MOE_PACK_GATE_UP && which != MOE_PACK_DOWN) return MOE_ERR_INVALID_ARG;
+    if (!scales) return MOE_ERR_INVALID_ARG;
+    if ((rc = check_ptr(w, 16)) || (rc = check_ptr(w_packed, 16)) || (rc = check_ptr(scales_packed, 8))) return rc;
+    const bool gu = which == MOE_PACK_GATE_UP;
+    const int64_t R = gu ? 2 * (int64_t)dims->I : dims->H, K = gu ? dims->H : dims->I;
+    const int64_t bytes = (int64_t)dims->E * R * (K / 2), sbytes = (int64_t)dims->E * R * (K / 32);
+    auto overlap = [](const void* a, int64_t na, const void* b, int64_t nb) {
+        const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+        return x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
+    };
+    if (overlap(w_packed, bytes, w, bytes) || overlap(w_packed, bytes, scales, sbytes) ||
+        overlap(scales_packed, sbytes, w, bytes) || overlap(scales_packed, sbytes, scales, sbytes) ||
+        overlap(w_packed, bytes, scales_packed, sbytes))
+        return MOE_ERR_INVALID_ARG;
+    return hip_status(moe::launch_mxfp4_pack(gu, dims->E, dims->I, dims->H, w, scales, w_packed, scales_packed,
+                                             static_cast<hipStream_t>(stream)));
 }
 
 int moe_mxfp4_fakequant(int64_t rows, int32_t cols, const void* w, void* out, void* stream)

@@ -39,7 +39,7 @@ hipError_t launch_select_permute_small(int T, int E, int k, const double* logits
 
 // ------------------------------------------------------------------ expert FFN
 struct FfnArgs {
-    int T, H, E, k, I, wfmt;
+    int T, H, E, k, I, wfmt;   // wfmt: 0 bf16, 1 MXFP4, 2 MXFP4 in the packed order
     const uint16_t* x;          // [T][H] (gate/up input, gathered)
     const int32_t* offsets;     // [E+1]
     const int32_t* sorted_pairs;  // [P]
@@ -57,6 +57,9 @@ struct FfnArgs {
     float* wg_out;              // [E][wg_M][wg_N]
 };
 hipError_t launch_gate_up_skinny(const FfnArgs& a, hipStream_t s);
+// The packed-MXFP4 skinny kernel addresses with 32-bit buffer offsets: true
+// when a's sizes fit them.
+bool skinny4_supported(const FfnArgs& a);
 hipError_t launch_down_skinny(const FfnArgs& a, hipStream_t s);
 hipError_t launch_gate_up_tiled(const FfnArgs& a, hipStream_t s);
 hipError_t launch_down_tiled(const FfnArgs& a, hipStream_t s);
@@ -88,5 +91,9 @@ hipError_t launch_router_bwd(int T, int H, int k, const uint16_t* wr, const int3
 int64_t mxfp4_quant_max_elems();
 hipError_t launch_mxfp4_quantize(const uint16_t* w, int64_t n_elems, uint8_t* packed, uint8_t* scales, hipStream_t s);
 hipError_t launch_mxfp4_fakequant(const uint16_t* w, int64_t n_elems, uint16_t* out, hipStream_t s);
+// Row-major MXFP4 expert tensor (E experts; gate/up [2I][H] or down [H][I]) ->
+// the packed MXFP4 order, bytes and scales.
+hipError_t launch_mxfp4_pack(bool gate_up, int E, int I, int H, const uint8_t* w, const uint8_t* s, uint8_t* wp,
+                             uint8_t* sp, hipStream_t st);
 
 }  // namespace moe

@@ -164,4 +164,49 @@ hipError_t launch_mxfp4_fakequant(const uint16_t* w, int64_t n_elems, uint16_t* 
     return launch_quant(true, w, n_elems, nullptr, nullptr, out, s);
 }
 
+// ---------------------------------------------------------------------------
+// Packed MXFP4 order.  A one-time reordering of an MXFP4 expert tensor for the
+// decode-regime kernel (it moves bytes and changes no value; the order is
+// documented with moe_mxfp4_pack).  One thread per 16-byte piece (one row over
+// one 32-element K-block): the read side walks the row-major tensor in order,
+// the piece and its scale byte are written to their packed positions.
+__global__ __launch_bounds__(256) void mxfp4_pack_kernel(int gate_up, int I, int R, int nkb, long long n_pieces,
+                                                        const u32x4* __restrict__ w, const uint8_t* __restrict__ s,
+                                                        uint8_t* __restrict__ wp, uint8_t* __restrict__ sp)
+{
+    const long long id = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (id >= n_pieces) return;
+    const int kb = (int)(id % nkb);
+    const long long er = id / nkb;  // expert * R + row
+    const long long e = er / R;
+    const int r = (int)(er % R);
+    int it, q;
+    if (gate_up) {  // item it: gate columns 16it..16it+15 in slots 0-15, the matching up rows in 16-31
+        const int n = r < I ? r : r - I;
+        it = n / 16;
+        q = n % 16 + (r < I ? 0 : 16);
+    } else {        // item it: rows 32it..32it+31
+        it = r / 32;
+        q = r % 32;
+    }
+    const int g = q >> 2, t = q & 3, c = kb >> 4, b = kb & 15;
+    const int nb = min(16, nkb - 16 * c);
+    const long long wo = e * R * (long long)nkb * 16 + (long long)it * 512 * nkb + 8192ll * c + 64 * g * nb +
+                         16 * (4 * b + t);
+    const long long so = e * R * (long long)nkb + (long long)it * 32 * nkb + 512ll * c + 8 * (4 * b + t) + g;
+    *reinterpret_cast<u32x4*>(wp + wo) = w[id];
+    sp[so] = s[id];
+}
+
+hipError_t launch_mxfp4_pack(bool gate_up, int E, int I, int H, const uint8_t* w, const uint8_t* s, uint8_t* wp,
+                             uint8_t* sp, hipStream_t st)
+{
+    const int R = gate_up ? 2 * I : H, K = gate_up ? H : I;
+    const long long n = (long long)E * R * (K / 32);
+    const long long grid = (n + 255) / 256;
+    hipLaunchKernelGGL(mxfp4_pack_kernel, dim3((unsigned)grid), dim3(256), 0, st, gate_up ? 1 : 0, I, R, K / 32, n,
+                       reinterpret_cast<const u32x4*>(w), s, wp, sp);
+    return hipGetLastError();
+}
+
 }  // namespace moe

@@ -23,11 +23,14 @@ def to_dev(a: np.ndarray, device="cuda") -> torch.Tensor:
 class GpuLayer:
     """Device copies of one synthetic layer plus the buffers of every stage."""
 
-    def __init__(self, layer: synth.Layer, path: int = moe.MOE_PATH_AUTO, device="cuda"):
+    def __init__(self, layer: synth.Layer, path: int = moe.MOE_PATH_AUTO, device="cuda", packed: bool = False):
+        """packed: MXFP4 weights are reordered on the device by moe_mxfp4_pack
+        and the layer runs with MOE_WFMT_MXFP4_PACKED."""
         c = layer.cfg
         self.cfg = c
         self.layer = layer
         self.device = device
+        self.wfmt = c.wfmt
         self.x = to_dev(layer.x, device)
         self.w_router = to_dev(layer.w_router, device)
         w = layer.weights
@@ -35,6 +38,9 @@ class GpuLayer:
         self.down = to_dev(w.down, device)
         self.gate_up_scale = to_dev(w.gate_up_scale, device) if w.wfmt == 1 else None
         self.down_scale = to_dev(w.down_scale, device) if w.wfmt == 1 else None
+        if packed:
+            assert w.wfmt == 1, "only MXFP4 weights have a packed order"
+            self.pack_weights()
         self.set_path(path)
         P = c.T * c.k
         i32 = dict(dtype=torch.int32, device=device)
@@ -47,9 +53,22 @@ class GpuLayer:
         self.y_sorted = torch.empty((P, c.H), dtype=torch.int16, device=device)
         self.y = torch.empty((c.T, c.H), dtype=torch.int16, device=device)
 
+    def pack_weights(self):
+        """Reorder the device MXFP4 weights into the packed order (C ABI)."""
+        c = self.cfg
+        d = moe.dims(c.T, c.H, c.E, c.k, c.I, moe.MOE_WFMT_MXFP4_PACKED)
+        out = []
+        for which, w, s in ((moe.MOE_PACK_GATE_UP, self.gate_up, self.gate_up_scale),
+                            (moe.MOE_PACK_DOWN, self.down, self.down_scale)):
+            wp, sp = torch.empty_like(w), torch.empty_like(s)
+            moe.moe_mxfp4_pack(d, which, w, s, wp, sp)
+            out += [wp, sp]
+        self.gate_up, self.gate_up_scale, self.down, self.down_scale = out
+        self.wfmt = moe.MOE_WFMT_MXFP4_PACKED
+
     def set_path(self, path: int):
         c = self.cfg
-        self.dims = moe.dims(c.T, c.H, c.E, c.k, c.I, c.wfmt, path)
+        self.dims = moe.dims(c.T, c.H, c.E, c.k, c.I, self.wfmt, path)
         self.ws_bytes = moe.moe_workspace_size(self.dims)
         self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=self.device)
         self.weights = moe.expert_weights(self.gate_up, self.down, self.gate_up_scale, self.down_scale)

@@ -42,7 +42,7 @@ def test_workspace_size_and_dim_validation(lib):
         moe.MOE_ERR_INVALID_ARG: [moe.dims(-1, 64, 4, 2, 64), moe.dims(4, 64, 4, 5, 64), moe.dims(4, 0, 4, 2, 64),
                                   moe.dims(4, 64, 4, 0, 64)],
         moe.MOE_ERR_UNSUPPORTED: [moe.dims(4, 64, 257, 2, 64), moe.dims(4, 64, 16, 9, 64), moe.dims(4, 48, 4, 2, 64),
-                                  moe.dims(4, 64, 4, 2, 80), moe.dims(4, 64, 4, 2, 64, wfmt=2),
+                                  moe.dims(4, 64, 4, 2, 80), moe.dims(4, 64, 4, 2, 64, wfmt=3),
                                   moe.dims(4, 64, 4, 2, 64, path=7)],
     }
     for code, ds in bad.items():
@@ -99,6 +99,43 @@ def test_quantizer_argument_errors_launch_nothing(lib):
     # an empty tensor is a no-op that succeeds even with null buffers
     assert q(0, 64, None, None, None, None) == moe.MOE_OK
     assert f(7, 0, None, None, None) == moe.MOE_OK
+
+
+def test_packed_format_argument_errors_launch_nothing(lib):
+    A, B, C, D = 0x10000, 0x200000, 0x400000, 0x600000  # fake, aligned, disjoint device addresses
+    byref = ctypes.byref
+    d = moe.dims(8, 64, 4, 2, 64, wfmt=moe.MOE_WFMT_MXFP4_PACKED)
+    pk = lib.moe_mxfp4_pack
+    assert pk(None, moe.MOE_PACK_GATE_UP, A, B, C, D, None) == moe.MOE_ERR_INVALID_ARG
+    assert pk(byref(d), 2, A, B, C, D, None) == moe.MOE_ERR_INVALID_ARG
+    assert pk(byref(d), moe.MOE_PACK_DOWN, A, None, C, D, None) == moe.MOE_ERR_INVALID_ARG
+    assert pk(byref(d), moe.MOE_PACK_DOWN, None, B, C, D, None) == moe.MOE_ERR_INVALID_ARG
+    assert pk(byref(d), moe.MOE_PACK_DOWN, A + 8, B, C, D, None) == moe.MOE_ERR_MISALIGNED
+    assert pk(byref(d), moe.MOE_PACK_DOWN, A, B, C + 8, D, None) == moe.MOE_ERR_MISALIGNED
+    assert pk(byref(d), moe.MOE_PACK_DOWN, A, B + 1, C, D + 4, None) == moe.MOE_ERR_MISALIGNED
+    # outputs overlapping an input or each other
+    assert pk(byref(d), moe.MOE_PACK_GATE_UP, A, B, A, D, None) == moe.MOE_ERR_INVALID_ARG
+    assert pk(byref(d), moe.MOE_PACK_GATE_UP, A, B, C, B, None) == moe.MOE_ERR_INVALID_ARG
+    assert pk(byref(d), moe.MOE_PACK_GATE_UP, A, B, C, C + 64, None) == moe.MOE_ERR_INVALID_ARG
+    dbad = moe.dims(8, 48, 4, 2, 64)
+    assert pk(byref(dbad), moe.MOE_PACK_GATE_UP, A, B, C, D, None) == moe.MOE_ERR_UNSUPPORTED
+    # the layer in the packed format: scales required, and 8-byte aligned
+    n = moe.moe_workspace_size(d)
+    W = moe.expert_weights(A, A)
+    assert _call(lib, "moe_gate_up", byref(d), A, A, A, byref(W), A, A, n, None) == moe.MOE_ERR_INVALID_ARG
+    W4 = moe.expert_weights(A, A, B + 4, B)
+    assert _call(lib, "moe_gate_up", byref(d), A, A, A, byref(W4), A, A, n, None) == moe.MOE_ERR_MISALIGNED
+    # the packed skinny kernel's 32-bit offsets: forced skinny beyond them is refused
+    big = moe.dims(1 << 19, 4096, 4, 2, 64, wfmt=moe.MOE_WFMT_MXFP4_PACKED, path=moe.MOE_PATH_SKINNY)
+    with pytest.raises(moe.MoeError) as ex:
+        moe.moe_workspace_size(big)
+    assert ex.value.code == moe.MOE_ERR_UNSUPPORTED
+    big.path = moe.MOE_PATH_AUTO  # the tiled path takes it
+    assert moe.moe_workspace_size(big) > 0
+    # an unknown format
+    with pytest.raises(moe.MoeError) as ex:
+        moe.moe_workspace_size(moe.dims(8, 64, 4, 2, 64, wfmt=3))
+    assert ex.value.code == moe.MOE_ERR_UNSUPPORTED
 
 
 def test_backward_argument_errors_launch_nothing(lib):

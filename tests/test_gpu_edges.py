@@ -24,13 +24,13 @@ def _layer(T, H, E, k, I, wfmt=0, seed=3, zipf=0.0):
     return synth.make_layer(cfg)
 
 
-def _check_forward(layer, path):
+def _check_forward(layer, path, packed=False):
     c = layer.cfg
-    print(f"[edge] {c.name} wfmt={c.wfmt} path={path}", flush=True)
+    print(f"[edge] {c.name} wfmt={c.wfmt} packed={packed} path={path}", flush=True)
     orc = oracle.get()
     tokens = np.arange(c.T, dtype=np.int32)
     y_ref, idx_ref, w_ref = orc.forward_tokens(layer.x, layer.w_router, layer.weights, c.k, c.I, tokens)
-    g = GpuLayer(layer, path)
+    g = GpuLayer(layer, path, packed=packed)
     g.forward()
     torch.cuda.synchronize()
     assert np.array_equal(g.topk_idx.cpu().numpy(), idx_ref)
@@ -47,9 +47,9 @@ def _check_forward(layer, path):
 @pytest.mark.parametrize("path", PATHS, ids=["skinny", "tiled"])
 @pytest.mark.parametrize("shape", [(37, 96, 5, 2, 160), (100, 64, 3, 3, 96), (1, 32, 8, 2, 32), (130, 160, 16, 4, 224)],
                          ids=lambda s: "T{}_H{}_E{}_k{}_I{}".format(*s))
-@pytest.mark.parametrize("wfmt", [0, 1], ids=["bf16", "mxfp4"])
+@pytest.mark.parametrize("wfmt", [0, 1, 2], ids=["bf16", "mxfp4", "mxfp4_packed"])
 def test_ragged_shapes(shape, path, wfmt):
-    _check_forward(_layer(*shape, wfmt=wfmt), path)
+    _check_forward(_layer(*shape, wfmt=min(wfmt, 1)), path, packed=wfmt == 2)
 
 
 @pytest.mark.parametrize("path", PATHS, ids=["skinny", "tiled"])

@@ -1,7 +1,8 @@
 """Host-streamed experts: the decode layer with its expert weights in pinned
 host memory (read over the host link by the same skinny kernels) gives the
 same output, bit for bit, as with the weights resident in HBM; that output
-is parity-checked against the oracle in test_gpu_parity.py."""
+is parity-checked against the oracle in test_gpu_parity.py.  The MXFP4
+layer is checked in the row-major and in the packed order."""
 from __future__ import annotations
 
 import pytest
@@ -15,15 +16,19 @@ from tests.host_weights import pinned_weights
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name", ["tiny", "20b_decode", "20b_mxfp4_decode"])
+@pytest.mark.parametrize("name", ["tiny", "20b_decode", "20b_mxfp4_decode", "20b_mxfp4_decode+packed"])
 def test_host_resident_weights_match_device_resident(name):
     print(f"host-resident weights {name}", flush=True)
-    layer = synth.make_layer(name)
-    g = GpuLayer(layer)
+    packed = name.endswith("+packed")
+    layer = synth.make_layer(name.split("+")[0])
+    g = GpuLayer(layer, packed=packed)
     g.forward()
     torch.cuda.synchronize()
     ref = g.y.clone()
-    parts = pinned_weights(layer.weights)
+    w = layer.weights
+    if packed:  # the device-packed weights, copied to the host
+        w = synth.Weights(1, *(t.cpu().numpy() for t in (g.gate_up, g.down, g.gate_up_scale, g.down_scale)))
+    parts = pinned_weights(w)
     if parts is None:
         pytest.skip("pinned host memory is not mapped for the device on this runtime")
     ptrs = [p.dev for p in parts] + [None, None]

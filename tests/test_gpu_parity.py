@@ -6,7 +6,8 @@ max|gpu - ref| <= 1e-2 * max|ref| (fp32 accumulation, bf16 storage).  Configs
 with more than 512 tokens are checked on a seeded sample of 512 tokens (each
 token's output depends on that token alone); routing and permutation are
 still checked on all tokens.  Both expert-FFN schedules (skinny and tiled)
-are forced on every config.
+are forced on every config; the MXFP4 configs also run with the weights in
+the packed order.
 """
 from __future__ import annotations
 
@@ -27,8 +28,12 @@ TOL = 1e-2
 W_TOL = 1e-5
 CHECK_TOKENS = 512
 
+# "+packed": the same MXFP4 layer with its weights reordered on the device by
+# moe_mxfp4_pack (MOE_WFMT_MXFP4_PACKED), against the oracle on the row-major
+# weights.
 CASES = ["tiny", "20b_decode"] + [f"120b_T{t}" for t in synth.SWEEP_120B] + [
-    "20b_prefill_zipf", "20b_mxfp4_decode", "20b_mxfp4_prefill"]
+    "20b_prefill_zipf", "20b_mxfp4_decode", "20b_mxfp4_prefill", "20b_mxfp4_decode+packed",
+    "20b_mxfp4_prefill+packed"]
 
 
 @functools.lru_cache(maxsize=1)
@@ -37,6 +42,7 @@ def _weights(cfg_name: str):
 
 
 def make_case(name: str) -> synth.Layer:
+    name = name.split("+")[0]
     if name.startswith("120b_T"):
         cfg = synth.CONFIGS["120b_sweep"].with_T(int(name[len("120b_T"):]))
         wkey = "120b_sweep"
@@ -62,7 +68,7 @@ class Case:
         self.tokens = synth.sample_tokens(c.T, CHECK_TOKENS, c.seed + 1)
         self.y, _, _, self.o, self.h = orc.forward_tokens(self.layer.x, self.layer.w_router, self.layer.weights, c.k,
                                                           c.I, self.tokens, want_pairs=True)
-        self.gpu = GpuLayer(self.layer)
+        self.gpu = GpuLayer(self.layer, packed=name.endswith("+packed"))
         # pair ids of the checked tokens, in (token, slot) order
         self.pairs = (self.tokens[:, None] * c.k + np.arange(c.k)[None, :]).ravel()
 

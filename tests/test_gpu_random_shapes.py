@@ -4,7 +4,8 @@ schedule, backward, and the quantiser), beyond the hand-picked edge cases.
 Each case draws T in [1, 300], H and I as 32 x [1, 12] (so tiles of every
 kernel have tails), E in [1, 40], k in [1, min(E, 8)], the weight format, the
 schedule (AUTO / SKINNY / TILED) and uniform or Zipf(1.1) routing, from a
-fixed seed; the parameters are printed before each case runs.  Same bar as
+fixed seed; the parameters are printed before each case runs.  The MXFP4
+cases run again with the weights in the packed order.  Same bar as
 the parity tests: routing bit-exact, weights within 1e-5, outputs and
 gradients within 1e-2 * max|ref|, quantiser bytes bit-exact.
 """
@@ -58,6 +59,22 @@ def test_random_forward(i):
     torch.cuda.synchronize()
     assert np.array_equal(g.topk_idx.cpu().numpy(), idx_ref)
     assert np.max(np.abs(g.topk_w.cpu().numpy() - w_ref)) <= 1e-5
+    e = rel_err(bf16_dev_to_f64(g.y), y_ref)
+    assert e <= TOL, e
+
+
+@pytest.mark.parametrize("i", [i for i in range(N_CASES) if CASES[i]["wfmt"] == 1])
+def test_random_forward_packed(i):
+    """The MXFP4 cases again with the weights in the packed order."""
+    c = CASES[i]
+    print(f"[random forward packed] {c}", flush=True)
+    layer = _layer(c)
+    y_ref, idx_ref, _ = oracle.get().forward_tokens(layer.x, layer.w_router, layer.weights, c["k"], c["I"],
+                                                    np.arange(c["T"], dtype=np.int32))
+    g = GpuLayer(layer, c["path"], packed=True)
+    g.forward()
+    torch.cuda.synchronize()
+    assert np.array_equal(g.topk_idx.cpu().numpy(), idx_ref)
     e = rel_err(bf16_dev_to_f64(g.y), y_ref)
     assert e <= TOL, e
 
