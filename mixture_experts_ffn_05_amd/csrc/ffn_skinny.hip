@@ -378,7 +378,8 @@ static hipError_t launch_skinny(const FfnArgs& a, hipStream_t s)
 // loaded: lane (b, t) loads token t's 32 bf16 at that K-block (64 B), where a
 // 16x16 MFMA would move 16 token columns whatever the count.  A wave item is
 // 32 weight rows (8 groups of 4; gate/up: 16 gate rows then the 16 matching
-// up rows) and 4 or 8 tokens per pass (TG groups of 4).  Per chunk lane
+// up rows) and 4 or 8 tokens per pass (TG groups of 4; a pass with at most 4
+// tokens multiplies only the first group).  Per chunk lane
 // (b, t) loads, from HBM straight into registers, the 16 bytes of E2M1 codes
 // of row 4g+t at its K-block for each group g with the 8 scale bytes, and
 // token 4*tg+t's activations; the E2M1 codes are decoded once and used by the
@@ -584,8 +585,11 @@ __device__ __forceinline__ uint32_t cvt_fp4_pair(uint32_t q, float scale)
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, scale, SEL));
 }
 
+// Multiply one chunk into the token groups' accumulators; groups after the
+// first only when `all` (a pass with at most 4 tokens skips them).  The E2M1
+// codes are decoded once per K step and feed every group.
 template <bool PACKED, int TG>
-__device__ __forceinline__ void s4_compute(const S4Buf<PACKED, TG>& b, f32x4 (&acc)[TG][S4_RG])
+__device__ __forceinline__ void s4_compute(const S4Buf<PACKED, TG>& b, bool all, f32x4 (&acc)[TG][S4_RG])
 {
     float sc[S4_RG];
 #pragma unroll
@@ -600,13 +604,19 @@ __device__ __forceinline__ void s4_compute(const S4Buf<PACKED, TG>& b, f32x4 (&a
             x0[tg] = (s & 1) ? xv.z : xv.x;
             x1[tg] = (s & 1) ? xv.w : xv.y;
         }
+        uint32_t a0[S4_RG], a1[S4_RG];
 #pragma unroll
         for (int g = 0; g < S4_RG; ++g) {
             const uint32_t q = b.w[g][s / 2];
-            const uint32_t a0 = (s & 1) ? cvt_fp4_pair<2>(q, sc[g]) : cvt_fp4_pair<0>(q, sc[g]);
-            const uint32_t a1 = (s & 1) ? cvt_fp4_pair<3>(q, sc[g]) : cvt_fp4_pair<1>(q, sc[g]);
+            a0[g] = (s & 1) ? cvt_fp4_pair<2>(q, sc[g]) : cvt_fp4_pair<0>(q, sc[g]);
+            a1[g] = (s & 1) ? cvt_fp4_pair<3>(q, sc[g]) : cvt_fp4_pair<1>(q, sc[g]);
+            acc[0][g] = mfma4(a0[g], a1[g], x0[0], x1[0], acc[0][g]);
+        }
+        if (TG > 1 && all) {
 #pragma unroll
-            for (int tg = 0; tg < TG; ++tg) acc[tg][g] = mfma4(a0, a1, x0[tg], x1[tg], acc[tg][g]);
+            for (int tg = 1; tg < TG; ++tg)
+#pragma unroll
+                for (int g = 0; g < S4_RG; ++g) acc[tg][g] = mfma4(a0[g], a1[g], x0[tg], x1[tg], acc[tg][g]);
         }
         __builtin_amdgcn_sched_barrier(0);  // decode one K step at a time (hoisting them all spills)
     }
@@ -675,11 +685,15 @@ __device__ __forceinline__ void s4_step(const FfnArgs& a, const S4Experts& x, in
     const S4Cursor c2 = s4_next<TG>(x, c1, K, n_items, tiles, nw);
     if constexpr (GATE_UP) s4_pairs<TG>(a, c2, p);
     s4_fetch<PACKED, TG, GATE_UP>(a, c1, xrow, K, nxt);
-    s4_compute<PACKED, TG>(cur, acc);
+    // groups past the pass's last token are loaded (as zeros) but not multiplied
+    const bool all_groups = TG == 1 || c0.M - c0.j0 > 4 * (TG - 1);
+    s4_compute<PACKED, TG>(cur, all_groups, acc);
     if (c1.item != c0.item || c1.j0 != c0.j0) {
         mfma_drain();
+        s4_epilogue<GATE_UP>(a, c0, 0, acc[0]);
+        if (all_groups)
 #pragma unroll
-        for (int tg = 0; tg < TG; ++tg) s4_epilogue<GATE_UP>(a, c0, tg, acc[tg]);
+            for (int tg = 1; tg < TG; ++tg) s4_epilogue<GATE_UP>(a, c0, tg, acc[tg]);
     }
     c0 = c1;
     c1 = c2;
