@@ -572,7 +572,15 @@ def main():
         return
     if args.only:  # "<config>" or "<config>+packed" (MXFP4 weights in the packed order)
         layer = synth.make_layer(args.only.split("+")[0])
-        tm = Timed(layer, 1, args.only.endswith("+packed"))
+        packed = args.only.endswith("+packed")
+        if layer.cfg.T <= 64:  # decode: rotated weight copies, as in the decode lines of the full run
+            tm, sec, stages, touched, total_b, gu_b = bench_decode(layer, args.steps, args.warmup, False, packed)
+            print(json.dumps({"workload": args.only, "tokens": layer.cfg.T, "steps": args.steps,
+                              "us_per_layer": round(sec * 1e6, 1), "tokens_per_s": round(layer.cfg.T / sec, 1),
+                              "touched_experts": touched, "hbm_frac": round(total_b / sec / 1e9 / HBM_PEAK_GBS, 4),
+                              "stages_us": {k: round(v, 1) for k, v in stages.items()}}))
+            return
+        tm = Timed(layer, 1, packed)
         sec = tm.run(args.steps, args.warmup)
         fl, _ = layer_flops(layer.cfg)
         print(json.dumps({"workload": args.only, "tokens": layer.cfg.T, "steps": args.steps,
