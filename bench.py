@@ -53,14 +53,18 @@ METRIC = "MoE-layer tokens/s + % HBM peak (decode, 16 tok) and % MFMA peak (pref
 MALL_BYTES = 256 << 20
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {"gate_up_skinny": "mixture_experts_ffn_05_amd/csrc/ffn_skinny.hip",
+                  "gate_up_skinny4": "mixture_experts_ffn_05_amd/csrc/ffn_skinny.hip",
                   "gate_up_tiled": "mixture_experts_ffn_05_amd/csrc/ffn_tiled.hip",
                   "mxfp4_quantize": "mixture_experts_ffn_05_amd/csrc/quant.hip"}
 TRAFFIC_FILES = {"gate_up_skinny": "skinny_gate_up_bf16_20b_decode_traffic.json",
+                 "gate_up_skinny4": "skinny4_gate_up_mxfp4_packed_20b_decode_traffic.json",
                  "mxfp4_quantize": "mxfp4_quantize_20b_gate_up_traffic.json"}
 # per counter summary: kernel-name pattern, workload, and the bench arguments of the counter runs
 TRAFFIC_RUNS = {
     "gate_up_skinny": ("skinny_kernel<0, true>", "20b decode, 16 tokens, bf16",
                        "--steps 20 --warmup 3 --no-secondary --no-cpu --copy-probe"),
+    "gate_up_skinny4": ("skinny4_kernel<true, 2, true>", "20b MXFP4 decode, 16 tokens, weights in the packed order",
+                        "--only 20b_mxfp4_decode+packed --steps 20 --warmup 3 --copy-probe"),
     "mxfp4_quantize": ("mxfp4_quant_kernel<false>", "MXFP4 quantiser on the 20b gate/up tensor [184320][2880] bf16",
                        "--only mxfp4_quantize --steps 20 --copy-probe"),
 }
@@ -502,10 +506,13 @@ def secondary(steps, graph=False):
     for packed in (False, True):
         layer = synth.make_layer("20b_mxfp4_decode")
         tm, sec, stages, touched, total_b, gu_b = bench_decode(layer, steps, 10, graph, packed)
-        out["20b_mxfp4_decode" + ("+packed" if packed else "")] = {
-            "tokens_per_s": round(layer.cfg.T / sec, 1), "us_per_layer": round(sec * 1e6, 1),
-            "touched_experts": touched, "hbm_frac": round(total_b / sec / 1e9 / HBM_PEAK_GBS, 4),
-            "stages_us": {k: round(v, 1) for k, v in stages.items()}}
+        rec = {"tokens_per_s": round(layer.cfg.T / sec, 1), "us_per_layer": round(sec * 1e6, 1),
+               "touched_experts": touched, "hbm_frac": round(total_b / sec / 1e9 / HBM_PEAK_GBS, 4),
+               "stages_us": {k: round(v, 1) for k, v in stages.items()}}
+        if packed:  # the gate/up kernel's measured HBM traffic against its algorithmic bytes
+            rec["gate_up_algorithmic_bytes"] = int(gu_b)
+            rec["gate_up_traffic_bytes"] = measured_traffic("gate_up_skinny4")
+        out["20b_mxfp4_decode" + ("+packed" if packed else "")] = rec
         del tm, layer
     base = synth.CONFIGS["120b_sweep"]
     w120 = synth.make_weights(base)
@@ -575,6 +582,8 @@ def main():
         packed = args.only.endswith("+packed")
         if layer.cfg.T <= 64:  # decode: rotated weight copies, as in the decode lines of the full run
             tm, sec, stages, touched, total_b, gu_b = bench_decode(layer, args.steps, args.warmup, False, packed)
+            if args.copy_probe:
+                copy_probe()
             print(json.dumps({"workload": args.only, "tokens": layer.cfg.T, "steps": args.steps,
                               "us_per_layer": round(sec * 1e6, 1), "tokens_per_s": round(layer.cfg.T / sec, 1),
                               "touched_experts": touched, "hbm_frac": round(total_b / sec / 1e9 / HBM_PEAK_GBS, 4),
