@@ -91,13 +91,13 @@ def measured_traffic(kernel: str):
 class Timed:
     """One workload on the device, with rotated weight copies."""
 
-    def __init__(self, layer, n_copies: int, packed: bool = False):
+    def __init__(self, layer, n_copies: int, packed: bool = False, weights_dev=None):
         import torch
 
         import mixture_experts_ffn_05_amd as moe
         from tests.gpu_layer import GpuLayer
         self.torch, self.moe = torch, moe
-        self.g = GpuLayer(layer, packed=packed)
+        self.g = GpuLayer(layer, packed=packed, weights_dev=weights_dev)
         c = layer.cfg
         g = self.g
         self.copies = [(g.gate_up, g.down, g.gate_up_scale, g.down_scale)]
@@ -210,15 +210,15 @@ def n_copies_for(cfg, touched_bytes):
     return max(4, min(16, int(4 * MALL_BYTES // max(touched_bytes, 1)) + 1))
 
 
-def bench_decode(layer, steps, warmup, graph=False, packed=False):
+def bench_decode(layer, steps, warmup, graph=False, packed=False, weights_dev=None):
     import torch
-    probe = Timed(layer, 1, packed)
+    probe = Timed(layer, 1, packed, weights_dev)
     probe.step(0)
     torch.cuda.synchronize()
     touched = probe.touched_experts()
     total_b, gu_b = layer_bytes(layer.cfg, touched)
     del probe
-    tm = Timed(layer, n_copies_for(layer.cfg, total_b), packed)
+    tm = Timed(layer, n_copies_for(layer.cfg, total_b), packed, weights_dev)
     sec = tm.run(steps, warmup, graph)
     stages = tm.stages(steps)
     return tm, sec, stages, touched, total_b, gu_b
@@ -483,6 +483,27 @@ def library_gemm_tflops(M: int = 32768, K: int = 2880, N: int = 5760, reps: int 
     return round(2.0 * M * K * N / sec / 1e12, 2)
 
 
+def device_mxfp4_weights(cfg, seed: int = 120):
+    """MXFP4 expert weights of cfg's shape made on the device: N(0, 0.02) bf16
+    draws from a seeded device generator, quantised by moe_mxfp4_quantize,
+    expert by expert (the host generator would take minutes at 128 experts)."""
+    import torch
+
+    import mixture_experts_ffn_05_amd as moe
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    out = []
+    for rows, cols in ((2 * cfg.I, cfg.H), (cfg.H, cfg.I)):
+        q = torch.empty((cfg.E, rows, cols // 2), dtype=torch.uint8, device="cuda")
+        sc = torch.empty((cfg.E, rows, cols // 32), dtype=torch.uint8, device="cuda")
+        for e in range(cfg.E):
+            w = (torch.randn((rows, cols), generator=g, device="cuda") * 0.02).to(torch.bfloat16).view(torch.int16)
+            moe.moe_mxfp4_quantize(rows, cols, w, q[e], sc[e])
+        out += [q, sc]
+    torch.cuda.synchronize()
+    return out[0], out[2], out[1], out[3]  # gate_up, down, gate_up_scale, down_scale
+
+
 def secondary(steps, graph=False):
     import synth
     out = {}
@@ -526,6 +547,23 @@ def secondary(steps, graph=False):
                          "gate_up_us": round(stages["gate_up"], 1)}
         del tm, layer
     out["120b_sweep"] = sweep
+    # the 120b shape with MXFP4 expert weights in the packed order (the pages' 120b is MXFP4)
+    import dataclasses
+    import torch
+    cfg4 = dataclasses.replace(base, name="120b_mxfp4", wfmt=1)
+    w4 = device_mxfp4_weights(cfg4)
+    sweep = {}
+    for T in synth.SWEEP_120B:
+        cfg = cfg4.with_T(T)
+        layer = synth.Layer(cfg, synth.make_x(cfg), synth.make_router(cfg), None)
+        tm, sec, stages, touched, total_b, gu_b = bench_decode(layer, steps, 10, graph, True, w4)
+        sweep[str(T)] = {"us_per_layer": round(sec * 1e6, 1), "touched_experts": touched,
+                         "hbm_frac": round(total_b / sec / 1e9 / HBM_PEAK_GBS, 4),
+                         "gate_up_us": round(stages["gate_up"], 1)}
+        del tm, layer
+    del w4
+    torch.cuda.empty_cache()
+    out["120b_mxfp4_packed_sweep"] = sweep
     out["mxfp4_quantize_20b_gate_up"] = bench_quantize(steps)
     out["backward_20b_prefill_zipf"] = bench_backward(steps)
     out["host_weights_20b_mxfp4_decode"] = bench_host_weights("20b_mxfp4_decode")

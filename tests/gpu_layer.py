@@ -23,9 +23,12 @@ def to_dev(a: np.ndarray, device="cuda") -> torch.Tensor:
 class GpuLayer:
     """Device copies of one synthetic layer plus the buffers of every stage."""
 
-    def __init__(self, layer: synth.Layer, path: int = moe.MOE_PATH_AUTO, device="cuda", packed: bool = False):
+    def __init__(self, layer: synth.Layer, path: int = moe.MOE_PATH_AUTO, device="cuda", packed: bool = False,
+                 weights_dev=None):
         """packed: MXFP4 weights are reordered on the device by moe_mxfp4_pack
-        and the layer runs with MOE_WFMT_MXFP4_PACKED."""
+        and the layer runs with MOE_WFMT_MXFP4_PACKED.  weights_dev: device
+        tensors (gate_up, down, gate_up_scale, down_scale) to use instead of
+        uploading layer.weights (in the layer's format, row-major)."""
         c = layer.cfg
         self.cfg = c
         self.layer = layer
@@ -33,13 +36,16 @@ class GpuLayer:
         self.wfmt = c.wfmt
         self.x = to_dev(layer.x, device)
         self.w_router = to_dev(layer.w_router, device)
-        w = layer.weights
-        self.gate_up = to_dev(w.gate_up, device)
-        self.down = to_dev(w.down, device)
-        self.gate_up_scale = to_dev(w.gate_up_scale, device) if w.wfmt == 1 else None
-        self.down_scale = to_dev(w.down_scale, device) if w.wfmt == 1 else None
+        if weights_dev is not None:
+            self.gate_up, self.down, self.gate_up_scale, self.down_scale = weights_dev
+        else:
+            w = layer.weights
+            self.gate_up = to_dev(w.gate_up, device)
+            self.down = to_dev(w.down, device)
+            self.gate_up_scale = to_dev(w.gate_up_scale, device) if w.wfmt == 1 else None
+            self.down_scale = to_dev(w.down_scale, device) if w.wfmt == 1 else None
         if packed:
-            assert w.wfmt == 1, "only MXFP4 weights have a packed order"
+            assert c.wfmt == 1, "only MXFP4 weights have a packed order"
             self.pack_weights()
         self.set_path(path)
         P = c.T * c.k
