@@ -238,7 +238,14 @@ def cpu_baseline(layer, min_seconds=10.0):
         el = time.perf_counter() - t0
         if el >= min_seconds or runs >= 20:
             break
+    cpu = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), cpu)
+    except OSError:
+        pass
     return {"value": round(runs * c.T / el, 3), "unit": "tokens/s", "cores": orc.max_threads(), "kind": "oracle",
+            "cpu_model": cpu,
             "sample": f"the whole {c.T}-token layer ({c.T * c.k} expert pairs), fp64 C oracle, {runs} run(s), "
                       f"{el:.1f} s"}
 

@@ -16,7 +16,7 @@ from tests.gpu_layer import GpuLayer
 
 pytestmark = pytest.mark.gpu
 
-CASES = ["tiny", "20b_decode", "20b_mxfp4_decode"]
+CASES = ["tiny", "20b_decode", "20b_mxfp4_decode", "20b_mxfp4_decode+packed"]
 
 
 def _eager(g: GpuLayer) -> torch.Tensor:
@@ -27,8 +27,8 @@ def _eager(g: GpuLayer) -> torch.Tensor:
 
 @pytest.mark.parametrize("name", CASES)
 def test_graph_replay_matches_eager(name):
-    layer = synth.make_layer(name)
-    g = GpuLayer(layer)
+    layer = synth.make_layer(name.split("+")[0])
+    g = GpuLayer(layer, packed=name.endswith("+packed"))
     ref = _eager(g)  # also warms up the library (kernel attributes, occupancy)
     x0 = g.x.clone()
     x1 = torch.roll(x0, shifts=1, dims=0).contiguous()  # different tokens, same values
