@@ -67,6 +67,15 @@ def test_max_experts_and_k(path):
     _check_forward(_layer(40, 64, 256, 8, 64), path)
 
 
+@pytest.mark.parametrize("path", PATHS, ids=["skinny", "tiled"])
+@pytest.mark.parametrize("shape", [(24, 64, 1, 1, 96), (19, 64, 4, 4, 64), (40, 64, 256, 8, 64)],
+                         ids=["E1", "k_equals_E", "E256_k8"])
+def test_packed_mxfp4_degenerate_and_max(shape, path):
+    """MXFP4 in the packed order at E = 1, k = E, and E = 256 with k = 8 (the
+    decode kernel's expert table spans all four groups of 64 experts)."""
+    _check_forward(_layer(*shape, wfmt=1), path, packed=True)
+
+
 def test_skewed_prefill_small():
     _check_forward(_layer(700, 64, 32, 4, 64, zipf=1.1), moe.MOE_PATH_TILED)
 
