@@ -30,10 +30,10 @@ CHECK_TOKENS = 512
 
 # "+packed": the same MXFP4 layer with its weights reordered on the device by
 # moe_mxfp4_pack (MOE_WFMT_MXFP4_PACKED), against the oracle on the row-major
-# weights.
+# weights; "@1": one token (single-stream decode, few touched experts).
 CASES = ["tiny", "20b_decode"] + [f"120b_T{t}" for t in synth.SWEEP_120B] + [
     "20b_prefill_zipf", "20b_mxfp4_decode", "20b_mxfp4_prefill", "20b_mxfp4_decode+packed",
-    "20b_mxfp4_prefill+packed"]
+    "20b_mxfp4_prefill+packed", "20b_mxfp4_decode@1+packed"]
 
 
 @functools.lru_cache(maxsize=1)
@@ -43,6 +43,11 @@ def _weights(cfg_name: str):
 
 def make_case(name: str) -> synth.Layer:
     name = name.split("+")[0]
+    if "@" in name:  # "<config>@T": the config's layer at T tokens
+        base, T = name.split("@")
+        cfg = synth.CONFIGS[base].with_T(int(T))
+        return synth.Layer(cfg, synth.make_x(cfg), synth.make_router(cfg),
+                           _weights("20b_mxfp4_decode" if cfg.wfmt == 1 else base))
     if name.startswith("120b_T"):
         cfg = synth.CONFIGS["120b_sweep"].with_T(int(name[len("120b_T"):]))
         wkey = "120b_sweep"
