@@ -63,7 +63,7 @@ TRAFFIC_FILES = {"gate_up_skinny": "skinny_gate_up_bf16_20b_decode_traffic.json"
 TRAFFIC_RUNS = {
     "gate_up_skinny": ("skinny_kernel<0, true>", "20b decode, 16 tokens, bf16",
                        "--steps 20 --warmup 3 --no-secondary --no-cpu --copy-probe"),
-    "gate_up_skinny4": ("skinny4_kernel<true, 2, true>", "20b MXFP4 decode, 16 tokens, weights in the packed order",
+    "gate_up_skinny4": ("skinny4_kernel<2, true>", "20b MXFP4 decode, 16 tokens, weights in the packed order",
                         "--only 20b_mxfp4_decode+packed --steps 20 --warmup 3 --copy-probe"),
     "mxfp4_quantize": ("mxfp4_quant_kernel<false>", "MXFP4 quantiser on the 20b gate/up tensor [184320][2880] bf16",
                        "--only mxfp4_quantize --steps 20 --copy-probe"),

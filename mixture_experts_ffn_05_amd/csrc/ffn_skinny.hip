@@ -386,10 +386,12 @@ static hipError_t launch_skinny(const FfnArgs& a, hipStream_t s)
 // TG token groups.  No LDS and no barrier: waves are independent.  After the
 // last chunk of a pass the 16 blocks' partial sums are added across lanes.
 //
-// Weights in the packed MXFP4 order (documented with moe_mxfp4_pack) make each
-// group's 16-byte pieces 1 KB of consecutive bytes per wave load and put a
-// lane's 8 scale bytes in one 8-byte word; in the row-major order a load
-// covers 4 rows x 256 B and the scales take 8 byte loads per chunk.
+// It reads weights in the packed MXFP4 order (documented with moe_mxfp4_pack),
+// which makes each group's 16-byte pieces 1 KB of consecutive bytes per wave
+// load and puts a lane's 8 scale bytes in one 8-byte word.  (Row-major MXFP4
+// weights are served by skinny_kernel above: read this way, each wave load
+// would cover 4 rows x 256 B and the scales would take 8 byte loads per chunk,
+// which streams slower.)
 constexpr int S4_RG = 8;                 // 4-row groups per item (32 rows)
 constexpr int S4_KB = 16;                // K-blocks per chunk, one per MFMA block
 constexpr int S4_KC = S4_KB * 32;        // K per chunk
@@ -403,11 +405,11 @@ struct S4Cursor {
     int e, it, s0, M, j0, kc;  // expert, item inside the expert, segment, token pass, K chunk
 };
 
-template <bool PACKED, int TG>
+template <int TG>
 struct S4Buf {
-    u32x4 w[S4_RG];                   // E2M1 codes of row 4g+t at this lane's K-block
-    uint32_t s[PACKED ? 2 : S4_RG];   // scale bytes: packed 8 per two words, else one per word
-    u32x4 x[TG][4];                   // token 4*tg+t: 32 bf16 at this lane's K-block
+    u32x4 w[S4_RG];    // E2M1 codes of row 4g+t at this lane's K-block
+    uint32_t s[2];     // the 8 scale bytes, one per group
+    u32x4 x[TG][4];    // token 4*tg+t: 32 bf16 at this lane's K-block
 };
 
 __device__ __forceinline__ f32x4 mfma4(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, f32x4 c)
@@ -483,16 +485,6 @@ __device__ __forceinline__ S4Cursor s4_next(const S4Experts& x, const S4Cursor& 
     return s4_item(x, c.item + nw, n_items, tiles);
 }
 
-// Row (inside the expert) that lane t supplies for group g of item it.
-template <bool GATE_UP>
-__device__ __forceinline__ int s4_row(const FfnArgs& a, int it, int g, int t)
-{
-    if constexpr (GATE_UP)  // groups 0-3: gate columns 16it..; groups 4-7: the matching up rows
-        return g < 4 ? 16 * it + 4 * g + t : a.I + 16 * it + 4 * (g - 4) + t;
-    else
-        return 32 * it + 4 * g + t;
-}
-
 // Pair indices of this lane's tokens in cursor c's pass (gate/up only), as
 // buffer loads so that they are in flight one step ahead of their use.
 template <int TG>
@@ -527,11 +519,11 @@ __device__ __forceinline__ uint32_t s4_xrow(const FfnArgs& a, const S4Cursor& c,
 // Issue chunk c's loads into b.  Past-the-end cursors and K-blocks past the
 // row read zeros through the buffer range checks, so every step issues the
 // same loads with no branch.
-template <bool PACKED, int TG, bool GATE_UP>
+template <int TG, bool GATE_UP>
 __device__ __forceinline__ void s4_fetch(const FfnArgs& a, const S4Cursor& c, const uint32_t (&xrow)[TG], int K,
-                                         S4Buf<PACKED, TG>& b)
+                                         S4Buf<TG>& b)
 {
-    const int lane = lane_id(), blk = lane >> 2, t = lane & 3;
+    const int lane = lane_id(), blk = lane >> 2;
     const int R = GATE_UP ? 2 * a.I : a.H;  // weight rows per expert
     const int nkb = K / 32;
     const bool live = c.item >= 0;
@@ -545,7 +537,7 @@ __device__ __forceinline__ void s4_fetch(const FfnArgs& a, const S4Cursor& c, co
         GATE_UP ? a.T * a.H * 2 : a.T * a.k * a.I * 2, 0x00020000);
     const int kb = c.kc / 32 + blk;  // this lane's K-block
     const bool kin = kb < nkb;
-    if constexpr (PACKED) {
+    {  // packed order: chunk cc of item it is [group][lane][16 B], its scales [lane][8 B]
         const int cc = c.kc / S4_KC, nb = min(S4_KB, nkb - S4_KB * cc);
         const uint32_t wb = (uint32_t)c.it * 512u * nkb + (uint32_t)cc * 8192u + 16u * lane;
 #pragma unroll
@@ -556,18 +548,6 @@ __device__ __forceinline__ void s4_fetch(const FfnArgs& a, const S4Cursor& c, co
         const uint2 sv = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(sr, kin ? sb : S4_OOB, 0, 2));
         b.s[0] = sv.x;
         b.s[1] = sv.y;
-    } else {
-#pragma unroll
-        for (int g = 0; g < S4_RG; ++g) {
-            const uint32_t row = (uint32_t)s4_row<GATE_UP>(a, c.it, g, t);
-            b.w[g] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                   wr, kin ? row * (uint32_t)(K / 2) + 16u * kb : S4_OOB, 0, 2));
-        }
-#pragma unroll
-        for (int g = 0; g < S4_RG; ++g) {
-            const uint32_t row = (uint32_t)s4_row<GATE_UP>(a, c.it, g, t);
-            b.s[g] = __builtin_amdgcn_raw_buffer_load_b8(sr, kin ? row * (uint32_t)nkb + kb : S4_OOB, 0, 2);
-        }
     }
 #pragma unroll
     for (int tg = 0; tg < TG; ++tg) {
@@ -588,13 +568,13 @@ __device__ __forceinline__ uint32_t cvt_fp4_pair(uint32_t q, float scale)
 // Multiply one chunk into the token groups' accumulators; groups after the
 // first only when `all` (a pass with at most 4 tokens skips them).  The E2M1
 // codes are decoded once per K step and feed every group.
-template <bool PACKED, int TG>
-__device__ __forceinline__ void s4_compute(const S4Buf<PACKED, TG>& b, bool all, f32x4 (&acc)[TG][S4_RG])
+template <int TG>
+__device__ __forceinline__ void s4_compute(const S4Buf<TG>& b, bool all, f32x4 (&acc)[TG][S4_RG])
 {
     float sc[S4_RG];
 #pragma unroll
     for (int g = 0; g < S4_RG; ++g)
-        sc[g] = e8m0_to_f32(PACKED ? (b.s[g / 4] >> (8 * (g % 4))) & 0xFFu : b.s[g]);
+        sc[g] = e8m0_to_f32((b.s[g / 4] >> (8 * (g % 4))) & 0xFFu);
 #pragma unroll
     for (int s = 0; s < 8; ++s) {  // 4 K per step: codes 4s..4s+3 = bytes 2s, 2s+1 of the lane's 16
         uint32_t x0[TG], x1[TG];
@@ -674,20 +654,20 @@ __device__ __forceinline__ void s4_epilogue(const FfnArgs& a, const S4Cursor& c,
 // One pipeline step: fetch cursor c1's chunk into nxt while multiplying c0's
 // (in cur), and finish c0's pass if c1 starts another.  p holds c1's pair
 // indices (loaded one step ago) and receives c2's.
-template <bool PACKED, int TG, bool GATE_UP>
+template <int TG, bool GATE_UP>
 __device__ __forceinline__ void s4_step(const FfnArgs& a, const S4Experts& x, int K, int n_items, int tiles, int nw,
-                                        S4Cursor& c0, S4Cursor& c1, uint32_t (&p)[TG], S4Buf<PACKED, TG>& cur,
-                                        S4Buf<PACKED, TG>& nxt, f32x4 (&acc)[TG][S4_RG])
+                                        S4Cursor& c0, S4Cursor& c1, uint32_t (&p)[TG], S4Buf<TG>& cur,
+                                        S4Buf<TG>& nxt, f32x4 (&acc)[TG][S4_RG])
 {
     uint32_t xrow[TG];
 #pragma unroll
     for (int tg = 0; tg < TG; ++tg) xrow[tg] = s4_xrow<GATE_UP>(a, c1, tg, p[tg]);
     const S4Cursor c2 = s4_next<TG>(x, c1, K, n_items, tiles, nw);
     if constexpr (GATE_UP) s4_pairs<TG>(a, c2, p);
-    s4_fetch<PACKED, TG, GATE_UP>(a, c1, xrow, K, nxt);
+    s4_fetch<TG, GATE_UP>(a, c1, xrow, K, nxt);
     // groups past the pass's last token are loaded (as zeros) but not multiplied
     const bool all_groups = TG == 1 || c0.M - c0.j0 > 4 * (TG - 1);
-    s4_compute<PACKED, TG>(cur, all_groups, acc);
+    s4_compute<TG>(cur, all_groups, acc);
     if (c1.item != c0.item || c1.j0 != c0.j0) {
         mfma_drain();
         s4_epilogue<GATE_UP>(a, c0, 0, acc[0]);
@@ -701,7 +681,7 @@ __device__ __forceinline__ void s4_step(const FfnArgs& a, const S4Experts& x, in
 
 // Persistent over items: wave w takes items w, w + nw, ... (item = touched
 // expert x 32-row tile; gate/up N = I, K = H; down N = H, K = I).
-template <bool PACKED, int TG, bool GATE_UP>
+template <int TG, bool GATE_UP>
 __global__ __launch_bounds__(S4_THREADS, 2) void skinny4_kernel(FfnArgs a)
 {
     const int K = GATE_UP ? a.H : a.I;
@@ -713,14 +693,14 @@ __global__ __launch_bounds__(S4_THREADS, 2) void skinny4_kernel(FfnArgs a)
     S4Cursor c0 = s4_item(x, w, n_items, tiles);
     if (c0.item < 0) return;  // uniform per wave
 
-    S4Buf<PACKED, TG> b0, b1;
+    S4Buf<TG> b0, b1;
     uint32_t p[TG], xrow[TG];
 #pragma unroll
     for (int tg = 0; tg < TG; ++tg) p[tg] = 0u;
     if constexpr (GATE_UP) s4_pairs<TG>(a, c0, p);
 #pragma unroll
     for (int tg = 0; tg < TG; ++tg) xrow[tg] = s4_xrow<GATE_UP>(a, c0, tg, p[tg]);
-    s4_fetch<PACKED, TG, GATE_UP>(a, c0, xrow, K, b0);
+    s4_fetch<TG, GATE_UP>(a, c0, xrow, K, b0);
     S4Cursor c1 = s4_next<TG>(x, c0, K, n_items, tiles, nw);
     if constexpr (GATE_UP) s4_pairs<TG>(a, c1, p);
     f32x4 acc[TG][S4_RG];
@@ -729,9 +709,9 @@ __global__ __launch_bounds__(S4_THREADS, 2) void skinny4_kernel(FfnArgs a)
 #pragma unroll
         for (int g = 0; g < S4_RG; ++g) acc[tg][g] = f32x4{0, 0, 0, 0};
     while (true) {  // two steps per iteration so the buffers swap roles without copies
-        s4_step<PACKED, TG, GATE_UP>(a, x, K, n_items, tiles, nw, c0, c1, p, b0, b1, acc);
+        s4_step<TG, GATE_UP>(a, x, K, n_items, tiles, nw, c0, c1, p, b0, b1, acc);
         if (c0.item < 0) break;
-        s4_step<PACKED, TG, GATE_UP>(a, x, K, n_items, tiles, nw, c0, c1, p, b1, b0, acc);
+        s4_step<TG, GATE_UP>(a, x, K, n_items, tiles, nw, c0, c1, p, b1, b0, acc);
         if (c0.item < 0) break;
     }
 }
@@ -745,37 +725,36 @@ bool skinny4_supported(const FfnArgs& a)
     return (long long)a.I * a.H < lim && (long long)a.T * a.H * 2 < lim && P * a.I * 2 < lim && P * 4 < lim;
 }
 
-template <bool PACKED, int TG, bool GATE_UP>
+template <int TG, bool GATE_UP>
 static hipError_t launch_skinny4_tg(const FfnArgs& a, hipStream_t s)
 {
-    static const int cap =
-        resident_blocks(reinterpret_cast<const void*>(&skinny4_kernel<PACKED, TG, GATE_UP>), S4_THREADS);
+    static const int cap = resident_blocks(reinterpret_cast<const void*>(&skinny4_kernel<TG, GATE_UP>), S4_THREADS);
     const int P = a.T * a.k;
     const int tiles = GATE_UP ? a.I / 16 : a.H / 32;
     const long long waves = (long long)(P < a.E ? P : a.E) * tiles;
     const long long blocks = (waves + S4_WPB - 1) / S4_WPB;
     const int grid = (int)(blocks < cap ? blocks : cap);
-    hipLaunchKernelGGL((skinny4_kernel<PACKED, TG, GATE_UP>), dim3(grid), dim3(S4_THREADS), 0, s, a);
+    hipLaunchKernelGGL((skinny4_kernel<TG, GATE_UP>), dim3(grid), dim3(S4_THREADS), 0, s, a);
     return hipGetLastError();
 }
 
 // An expert sees at most T tokens: one 4-token group covers T <= 4, else two
 // groups (8 tokens per pass over the weights).
-template <bool PACKED, bool GATE_UP>
+template <bool GATE_UP>
 static hipError_t launch_skinny4(const FfnArgs& a, hipStream_t s)
 {
-    return a.T <= 4 ? launch_skinny4_tg<PACKED, 1, GATE_UP>(a, s) : launch_skinny4_tg<PACKED, 2, GATE_UP>(a, s);
+    return a.T <= 4 ? launch_skinny4_tg<1, GATE_UP>(a, s) : launch_skinny4_tg<2, GATE_UP>(a, s);
 }
 
 hipError_t launch_gate_up_skinny(const FfnArgs& a, hipStream_t s)
 {
-    if (a.wfmt == 2) return launch_skinny4<true, true>(a, s);
+    if (a.wfmt == 2) return launch_skinny4<true>(a, s);
     return a.wfmt == 0 ? launch_skinny<0, true>(a, s) : launch_skinny<1, true>(a, s);
 }
 
 hipError_t launch_down_skinny(const FfnArgs& a, hipStream_t s)
 {
-    if (a.wfmt == 2) return launch_skinny4<true, false>(a, s);
+    if (a.wfmt == 2) return launch_skinny4<false>(a, s);
     return a.wfmt == 0 ? launch_skinny<0, false>(a, s) : launch_skinny<1, false>(a, s);
 }
 
