@@ -75,6 +75,60 @@ def source_digest(rel: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
+CSRC = "mixture_experts_ffn_05_amd/csrc"
+HEADLINE_TRACE = "bench_20b_decode_kernel_stats.txt"
+
+
+def sources_digest() -> str:
+    """One digest over every kernel source file (a trace summary is current
+    only while this matches the one it was taken on)."""
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, CSRC)
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(d, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def summarize_trace(run_dir: str, out_path: str, title: str, command: str):
+    """Text summary of a `rocprofv3 --kernel-trace --stats` run directory:
+    per-kernel calls and average/min/max duration, with the command that made
+    it and the digest of the kernel sources it ran."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(run_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {run_dir}")
+    rows = list(csv.DictReader(open(files[0])))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    lines = [title, "", "command (repo root, MI355X):", "  " + command,
+             f"kernel sources digest: {sources_digest()}", "",
+             f"{'kernel':<72}{'calls':>8}{'avg us':>10}{'min us':>10}{'max us':>10}{'% time':>8}"]
+    for r in rows:
+        lines.append(f"{r['Name'][:70]:<72}{int(r['Calls']):>8}{float(r['AverageNs']) / 1e3:>10.2f}"
+                     f"{float(r['MinNs']) / 1e3:>10.2f}{float(r['MaxNs']) / 1e3:>10.2f}{float(r['Percentage']):>8.2f}")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def trace_mean_us(pattern: str, summary: str = HEADLINE_TRACE):
+    """Average duration (us) of the kernel matching `pattern` in a committed
+    trace summary, if it was taken on the current kernel sources (else None)."""
+    path = os.path.join(PROFILE_DIR, summary)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read().splitlines()
+    if f"kernel sources digest: {sources_digest()}" not in text:
+        return None
+    for ln in text:
+        if pattern in ln:
+            parts = ln[72:].split()
+            return float(parts[1])
+    return None
+
+
 def measured_traffic(kernel: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if
     it was taken on the current source of the kernel (else None)."""
@@ -88,6 +142,16 @@ def measured_traffic(kernel: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def device_layer(layer, packed: bool = False, weights_dev=None):
+    """The package's DeviceLayer for a synthetic layer (synth.Layer)."""
+    from mixture_experts_ffn_05_amd.layer import DeviceLayer
+    c, w = layer.cfg, layer.weights
+    host = {} if weights_dev is not None else dict(gate_up=w.gate_up, down=w.down, gate_up_scale=w.gate_up_scale,
+                                                   down_scale=w.down_scale)
+    return DeviceLayer(c.T, c.H, c.E, c.k, c.I, c.wfmt, layer.x, layer.w_router, packed=packed,
+                       weights_dev=weights_dev, **host)
+
+
 class Timed:
     """One workload on the device, with rotated weight copies."""
 
@@ -95,9 +159,8 @@ class Timed:
         import torch
 
         import mixture_experts_ffn_05_amd as moe
-        from tests.gpu_layer import GpuLayer
         self.torch, self.moe = torch, moe
-        self.g = GpuLayer(layer, packed=packed, weights_dev=weights_dev)
+        self.g = device_layer(layer, packed=packed, weights_dev=weights_dev)
         c = layer.cfg
         g = self.g
         self.copies = [(g.gate_up, g.down, g.gate_up_scale, g.down_scale)]
@@ -146,9 +209,13 @@ class Timed:
         torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
 
-    def run(self, steps: int, warmup: int, graph: bool = False):
+    def run(self, steps: int, warmup: int, graph: bool = False, repeats: int = 1):
         """Seconds per layer step (moe_forward, eager launches or a HIP graph
-        replay of the same launches), inputs resident in HBM."""
+        replay of the same launches), inputs resident in HBM: `warmup` untimed
+        steps, then `repeats` windows of exactly `steps` steps, each
+        bracketed by device synchronisations; the median window.  The
+        per-window figures are kept in self.windows."""
+        import statistics
         torch = self.torch
         if graph:
             self.capture()
@@ -157,12 +224,15 @@ class Timed:
             go = self.forward
         for i in range(warmup):
             go(i)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(steps):
-            go(i)
-        torch.cuda.synchronize()
-        return (time.perf_counter() - t0) / steps
+        self.windows = []
+        for _ in range(repeats):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i in range(steps):
+                go(i)
+            torch.cuda.synchronize()
+            self.windows.append((time.perf_counter() - t0) / steps)
+        return statistics.median(self.windows)
 
     def stages(self, steps: int, warmup: int = 3):
         """Mean microseconds of each stage entry point, from HIP events
@@ -210,7 +280,7 @@ def n_copies_for(cfg, touched_bytes):
     return max(4, min(16, int(4 * MALL_BYTES // max(touched_bytes, 1)) + 1))
 
 
-def bench_decode(layer, steps, warmup, graph=False, packed=False, weights_dev=None):
+def bench_decode(layer, steps, warmup, graph=False, packed=False, weights_dev=None, repeats=1):
     import torch
     probe = Timed(layer, 1, packed, weights_dev)
     probe.step(0)
@@ -219,35 +289,75 @@ def bench_decode(layer, steps, warmup, graph=False, packed=False, weights_dev=No
     total_b, gu_b = layer_bytes(layer.cfg, touched)
     del probe
     tm = Timed(layer, n_copies_for(layer.cfg, total_b), packed, weights_dev)
-    sec = tm.run(steps, warmup, graph)
+    sec = tm.run(steps, warmup, graph, repeats)
     stages = tm.stages(steps)
     return tm, sec, stages, touched, total_b, gu_b
 
 
-def cpu_baseline(layer, min_seconds=10.0):
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            return next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "unknown CPU")
+    except OSError:
+        return "unknown CPU"
+
+
+def _time_oracle(fn, min_seconds: float, max_runs: int = 20):
+    """Runs fn until min_seconds have passed (at least once); (runs, seconds)."""
+    runs, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        runs += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds or runs >= max_runs:
+            return runs, el
+
+
+def cpu_baseline(layer, min_seconds: float = 8.0, prefill_tokens: int = 64):
+    """The fp64 C oracle, as it stands, on this host's cores:
+      - the whole decode layer (headline workload) on all the cores the oracle's
+        OpenMP runtime uses, and on one core;
+      - the two prefill configs (8192-token Zipf bf16, 32768-token MXFP4): the
+        router over all tokens, then the expert FFN and combine of a seeded
+        sample of `prefill_tokens` tokens (every token's output depends on that
+        token alone), extrapolated to the whole batch (labelled as such)."""
     import numpy as np
 
     import oracle
+    import synth
     orc = oracle.get()
+    cores = orc.max_threads()
     c = layer.cfg
     tokens = np.arange(c.T, dtype=np.int32)
-    runs, t0 = 0, time.perf_counter()
-    while True:
-        orc.forward_tokens(layer.x, layer.w_router, layer.weights, c.k, c.I, tokens)
-        runs += 1
-        el = time.perf_counter() - t0
-        if el >= min_seconds or runs >= 20:
-            break
-    cpu = "unknown CPU"
-    try:
-        with open("/proc/cpuinfo") as f:
-            cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), cpu)
-    except OSError:
-        pass
-    return {"value": round(runs * c.T / el, 3), "unit": "tokens/s", "cores": orc.max_threads(), "kind": "oracle",
-            "cpu_model": cpu,
-            "sample": f"the whole {c.T}-token layer ({c.T * c.k} expert pairs), fp64 C oracle, {runs} run(s), "
-                      f"{el:.1f} s"}
+    fwd = lambda thr: orc.forward_tokens(layer.x, layer.w_router, layer.weights, c.k, c.I, tokens,  # noqa: E731
+                                         threads=thr)
+    runs, el = _time_oracle(lambda: fwd(cores), min_seconds)
+    runs1, el1 = _time_oracle(lambda: fwd(1), 0.0, 1)
+    out = {"value": round(runs * c.T / el, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+           "cpu_model": _cpu_model(),
+           "sample": f"the whole {c.T}-token decode layer ({c.T * c.k} expert pairs), fp64 C oracle, {runs} run(s) "
+                     f"on {cores} threads, {el:.1f} s",
+           "single_core": {"value": round(runs1 * c.T / el1, 3), "unit": "tokens/s", "cores": 1,
+                           "sample": f"the same layer on one thread, {runs1} run(s), {el1:.1f} s"}}
+    for name in ("20b_prefill_zipf", "20b_mxfp4_prefill"):
+        pl = synth.make_layer(name)
+        pc = pl.cfg
+        t0 = time.perf_counter()
+        orc.route(pl.x, pl.w_router, pc.k, threads=cores)
+        t_route = time.perf_counter() - t0
+        sub = synth.sample_tokens(pc.T, prefill_tokens, pc.seed + 1)
+        t0 = time.perf_counter()
+        orc.forward_tokens(pl.x, pl.w_router, pl.weights, pc.k, pc.I, sub, threads=cores)
+        t_sub = time.perf_counter() - t0
+        per_tok = t_sub / len(sub)
+        out[name] = {"route_all_tokens_s": round(t_route, 2), "subset_tokens": len(sub), "subset_s": round(t_sub, 2),
+                     "us_per_token": round(per_tok * 1e6, 1),
+                     "extrapolated_tokens_per_s": round(1.0 / per_tok, 3),
+                     "extrapolated_us_per_layer": round(per_tok * pc.T * 1e6 + t_route * 1e6, 0),
+                     "cores": cores, "note": "expert FFN time extrapolated from the sample to all "
+                                             f"{pc.T} tokens; router timed on all tokens"}
+        del pl
+    return out
 
 
 COPY_PROBE_BYTES = 1 << 30
@@ -386,7 +496,7 @@ def bench_backward(steps: int, name: str = "20b_prefill_zipf"):
 
     import mixture_experts_ffn_05_amd as moe
     import synth
-    from tests.gpu_layer import to_dev
+    from mixture_experts_ffn_05_amd.layer import to_dev
     layer = synth.make_layer(name)
     c = layer.cfg
     P = c.T * c.k
@@ -436,14 +546,13 @@ def bench_host_weights(name: str = "20b_mxfp4_decode", reps: int = 5, packed: bo
 
     import mixture_experts_ffn_05_amd as moe
     import synth
-    from tests.gpu_layer import GpuLayer
-    from tests.host_weights import pinned_weights
+    from mixture_experts_ffn_05_amd.host_weights import pinned_weights
     layer = synth.make_layer(name)
-    g = GpuLayer(layer, packed=packed)
-    w = layer.weights
-    if packed:
-        w = synth.Weights(1, *(t.cpu().numpy() for t in (g.gate_up, g.down, g.gate_up_scale, g.down_scale)))
-    parts = pinned_weights(w)
+    g = device_layer(layer, packed=packed)
+    host = [t.cpu().numpy() for t in (g.gate_up, g.down)]  # the device's (possibly packed) bytes
+    if g.gate_up_scale is not None:
+        host += [g.gate_up_scale.cpu().numpy(), g.down_scale.cpu().numpy()]
+    parts = pinned_weights(*host)
     if parts is None:
         return {"workload": name, "skipped": "pinned host memory not mapped"}
     ptrs = [p.dev for p in parts] + [None, None]
@@ -490,27 +599,6 @@ def library_gemm_tflops(M: int = 32768, K: int = 2880, N: int = 5760, reps: int 
     return round(2.0 * M * K * N / sec / 1e12, 2)
 
 
-def device_mxfp4_weights(cfg, seed: int = 120):
-    """MXFP4 expert weights of cfg's shape made on the device: N(0, 0.02) bf16
-    draws from a seeded device generator, quantised by moe_mxfp4_quantize,
-    expert by expert (the host generator would take minutes at 128 experts)."""
-    import torch
-
-    import mixture_experts_ffn_05_amd as moe
-    g = torch.Generator(device="cuda")
-    g.manual_seed(seed)
-    out = []
-    for rows, cols in ((2 * cfg.I, cfg.H), (cfg.H, cfg.I)):
-        q = torch.empty((cfg.E, rows, cols // 2), dtype=torch.uint8, device="cuda")
-        sc = torch.empty((cfg.E, rows, cols // 32), dtype=torch.uint8, device="cuda")
-        for e in range(cfg.E):
-            w = (torch.randn((rows, cols), generator=g, device="cuda") * 0.02).to(torch.bfloat16).view(torch.int16)
-            moe.moe_mxfp4_quantize(rows, cols, w, q[e], sc[e])
-        out += [q, sc]
-    torch.cuda.synchronize()
-    return out[0], out[2], out[1], out[3]  # gate_up, down, gate_up_scale, down_scale
-
-
 def secondary(steps, graph=False):
     import synth
     out = {}
@@ -554,16 +642,16 @@ def secondary(steps, graph=False):
                          "gate_up_us": round(stages["gate_up"], 1)}
         del tm, layer
     out["120b_sweep"] = sweep
+    del w120
     # the 120b shape with MXFP4 expert weights in the packed order (the pages' 120b is MXFP4)
-    import dataclasses
     import torch
-    cfg4 = dataclasses.replace(base, name="120b_mxfp4", wfmt=1)
-    w4 = device_mxfp4_weights(cfg4)
+    cfg4 = synth.CONFIGS["120b_mxfp4_sweep"]
+    w4 = synth.make_weights(cfg4)
     sweep = {}
     for T in synth.SWEEP_120B:
         cfg = cfg4.with_T(T)
-        layer = synth.Layer(cfg, synth.make_x(cfg), synth.make_router(cfg), None)
-        tm, sec, stages, touched, total_b, gu_b = bench_decode(layer, steps, 10, graph, True, w4)
+        layer = synth.Layer(cfg, synth.make_x(cfg), synth.make_router(cfg), w4)
+        tm, sec, stages, touched, total_b, gu_b = bench_decode(layer, steps, 10, graph, True)
         sweep[str(T)] = {"us_per_layer": round(sec * 1e6, 1), "touched_experts": touched,
                          "hbm_frac": round(total_b / sec / 1e9 / HBM_PEAK_GBS, 4),
                          "gate_up_us": round(stages["gate_up"], 1)}
@@ -581,13 +669,17 @@ def secondary(steps, graph=False):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--repeats", type=int, default=5,
+                    help="timed windows of --steps steps each; the headline is their median")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe", action="store_true", help="also launch a copy kernel of known size")
     ap.add_argument("--graph", action="store_true", help="replay each layer step as a captured HIP graph")
     ap.add_argument("--write-traffic", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT_JSON"))
+    ap.add_argument("--summarize-trace", nargs=4, metavar=("RUN_DIR", "OUT_TXT", "TITLE", "COMMAND"),
+                    help="write a text summary of a rocprofv3 --kernel-trace --stats run")
     ap.add_argument("--traffic-kernel", default="gate_up_skinny", choices=sorted(TRAFFIC_RUNS),
                     help="which kernel --write-traffic summarises")
     ap.add_argument("--only", metavar="WORKLOAD",
@@ -596,6 +688,9 @@ def main():
     args = ap.parse_args()
     if args.write_traffic:
         write_traffic(*args.write_traffic, kernel=args.traffic_kernel)
+        return
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -645,7 +740,9 @@ def main():
 
     layer = synth.make_layer("20b_decode")
     c = layer.cfg
-    tm, sec, stages, touched, total_b, gu_b = bench_decode(layer, args.steps, args.warmup, args.graph)
+    tm, sec, stages, touched, total_b, gu_b = bench_decode(layer, args.steps, args.warmup, args.graph,
+                                                           repeats=args.repeats)
+    windows = [round(w * 1e3, 4) for w in tm.windows]
     gu_us = stages["gate_up"]
     achieved = gu_b / (gu_us * 1e-6) / 1e9
     rec = {
@@ -656,6 +753,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(sec * 1e3, 4),
+        "ms_per_step_windows": windows,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -673,7 +771,10 @@ def main():
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic("gate_up_skinny"),
-                     "algorithmic_bytes_per_launch": gu_b, "mean_launch_us": round(gu_us, 2)},
+                     "algorithmic_bytes_per_launch": gu_b, "mean_launch_us": round(gu_us, 2),
+                     "mean_launch_us_source": "HIP events around the launch on its stream, this run",
+                     "mean_launch_us_trace": trace_mean_us(DOMINANT_KERNEL),
+                     "trace_summary": "profiles/" + HEADLINE_TRACE},
     }
     # the same layer step replayed from a captured HIP graph, for reference (eager launches are the headline)
     sec_other = tm.run(args.steps, args.warmup, graph=not args.graph)

@@ -139,15 +139,22 @@ int moe_workspace_size(const moe_dims* dims, size_t* bytes);
 
 /* Router (logits, top-k selection, softmax over the k selected).
  * Reads x, w_router; writes topk_idx [T][k], topk_w [T][k].
- * Selection is made on logits equal to the exactly-rounded sum (decided in
- * fp64), so indices match a double-precision reference bit for bit. */
+ * Each logit is an fp64 sum of the H bf16 x bf16 products (each exact in
+ * fp64); the summation order differs between kernels, so a logit may differ
+ * from the exact sum by up to about H * 2^-53 * sum_h |x[h] * w[h]|.  Indices
+ * therefore match any double-precision reference unless two of a token's
+ * logits lie that close together; exactly equal logits (duplicated router
+ * rows) stay exactly equal and go to the lower index.  A NaN logit ranks
+ * below every number (as -infinity), so the k indices of a token are always
+ * distinct and in [0, E): a token whose logits are all NaN (a NaN in its x
+ * row) gets experts 0..k-1 and NaN weights; other tokens are unaffected. */
 int moe_route(const moe_dims* dims, const void* x, const void* w_router, int32_t* topk_idx, float* topk_w,
               void* workspace, size_t workspace_bytes, void* stream);
 
 /* Permutation of the P pairs into expert-contiguous segments (stable counting
  * sort by expert).  Reads topk_idx; writes expert_offsets [E+1],
  * sorted_pairs [P], pair_rank [P].  topk_idx values outside [0, E) are
- * undefined behaviour (the router never produces them). */
+ * undefined behaviour (moe_route never produces them, whatever its input). */
 int moe_permute(const moe_dims* dims, const int32_t* topk_idx, int32_t* expert_offsets, int32_t* sorted_pairs,
                 int32_t* pair_rank, void* workspace, size_t workspace_bytes, void* stream);
 

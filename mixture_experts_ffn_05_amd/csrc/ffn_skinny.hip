@@ -2,10 +2,11 @@
 // layer is a stream over the touched experts' weights and runs at the rate
 // HBM delivers them.
 //
-// The pages show why this regime matters: with gpt-oss-120b at 12-16 streams
-// each expert sees about one token per step, and a kernel that switches from
-// mat-vec to dequantise-then-mat-mat above 8 tokens becomes ~5x slower per
-// call ("hearth-lean-loomed-v1", section "Why 12-16 streams can be slow on
+// The pages show why this regime matters: routing top-4 of 128 experts for
+// 12 to 16 concurrent streams leaves roughly one token per expert per decode
+// step, and the engine they measure loses about 5x per expert call when it
+// leaves its mat-vec kernel for a dequantise-then-mat-mat one above 8 tokens
+// ("hearth-lean-loomed-v1", section "Why 12-16 streams can be slow on
 // Vulkan").  Here one kernel serves any token count: the tokens are the
 // 16-wide N side of a bf16 MFMA (v_mfma_f32_16x16x32_bf16) whose M side is 16
 // weight rows, so 1..16 tokens per expert cost the same weight traffic and

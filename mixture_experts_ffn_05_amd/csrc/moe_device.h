@@ -173,6 +173,14 @@ __device__ __forceinline__ int locate_m_tile(const int32_t* __restrict__ offsets
 // taken is): larger logit first, an exactly equal logit goes to the lower
 // expert index; weights = softmax over the k selected logits.
 
+// The value a logit is ranked and weighted by: a NaN logit (a NaN in the
+// token's row or in the expert's router row) ranks below every number, as
+// -infinity, so selection always yields k distinct experts in [0, E); a token
+// whose logits are all NaN gets experts 0..k-1 by the tie rule and NaN
+// weights.  (The pages say nothing of non-finite inputs; this is the reading
+// taken.)
+__device__ __forceinline__ double rank_key(double v) { return __builtin_isnan(v) ? -__builtin_inf() : v; }
+
 // Does candidate (v, i) rank before (bv, bi)?  Larger logit first, then the
 // lower expert index.
 __device__ __forceinline__ bool ranks_before(double v, int i, double bv, int bi)
@@ -196,7 +204,7 @@ __device__ __forceinline__ void wave_topk_softmax_rank(const double* row, int E,
                                                        float* __restrict__ w_out, TopkScratch& sc)
 {
     const int e = lane_id();
-    const double v = e < E ? row[e] : -__builtin_inf();
+    const double v = e < E ? rank_key(row[e]) : -__builtin_inf();
     sc.v[e] = v;
     __builtin_amdgcn_wave_barrier();
     int rank = 0;
@@ -233,7 +241,7 @@ __device__ __forceinline__ void wave_topk_softmax(const double* row, int E, int 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int e = lane + WAVE * i;
-        v[i] = e < E ? row[e] : -__builtin_inf();
+        v[i] = e < E ? rank_key(row[e]) : -__builtin_inf();
     }
     uint32_t taken = 0;
     double sel_v[8];

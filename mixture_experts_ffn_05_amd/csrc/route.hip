@@ -176,8 +176,13 @@ __global__ __launch_bounds__(RL_WAVES * WAVE) void router_logits_mfma_kernel(int
     } else {
         // Token t0 + 4i + g is held by the 16 lanes of group g (expert 16j + r
         // in element i of tile j): k rounds of arg-max within the group
-        // (largest logit, an exactly equal one to the lower index), then the
-        // softmax over the k, in the same arithmetic as router_select_kernel.
+        // (largest logit, an exactly equal one to the lower index; NaN ranks
+        // as -infinity), then the softmax over the k, in the same arithmetic
+        // as router_select_kernel.
+#pragma unroll
+        for (int j = 0; j < RL_ET; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[j][i] = rank_key(v[j][i]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int t = t0 + 4 * i + g;

@@ -129,16 +129,31 @@ static void router_logits_one(int H, int E, const uint16_t* xrow, const uint16_t
     }
 }
 
+/* The value a logit is ranked and weighted by.  The pages say nothing about
+ * non-finite inputs; the reading taken: a NaN logit (a NaN in the token's
+ * row or in the expert's router row) ranks below every number, as -infinity,
+ * so selection always yields k distinct experts.  A token whose logits are
+ * all NaN gets experts 0..k-1 by the tie rule, and NaN weights. */
+static double rank_key(double v)
+{
+#if ORC_PLANT == 8
+    return v; /* planted: NaN logits compared raw */
+#else
+    return isnan(v) ? -INFINITY : v;
+#endif
+}
+
 /* Does expert a come before expert b in routing order?  Larger logit first;
  * an exactly equal logit puts the lower index first. */
 static int route_before(const double* l, int a, int b)
 {
+    const double la = rank_key(l[a]), lb = rank_key(l[b]);
 #if ORC_PLANT == 2
-    if (l[a] == l[b]) return a > b; /* planted: ties go to the higher index */
+    if (la == lb) return a > b; /* planted: ties go to the higher index */
 #else
-    if (l[a] == l[b]) return a < b;
+    if (la == lb) return a < b;
 #endif
-    return l[a] > l[b];
+    return la > lb;
 }
 
 /* Order all E experts by routing order (insertion sort), keep the first k as
@@ -153,15 +168,15 @@ static void select_topk_one(int E, int k, const double* l, int32_t* idx, double*
         }
         order[pos] = e;
     }
-    double lmax = l[order[0]];
+    double lmax = rank_key(l[order[0]]);
     double z = 0.0;
-    for (int j = 0; j < k; ++j) z += exp(l[order[j]] - lmax);
+    for (int j = 0; j < k; ++j) z += exp(rank_key(l[order[j]]) - lmax);
     for (int j = 0; j < k; ++j) {
         idx[j] = order[j];
 #if ORC_PLANT == 7
-        w[j] = exp(l[order[j]] - lmax); /* planted: weights not normalised */
+        w[j] = exp(rank_key(l[order[j]]) - lmax); /* planted: weights not normalised */
 #else
-        w[j] = exp(l[order[j]] - lmax) / z;
+        w[j] = exp(rank_key(l[order[j]]) - lmax) / z;
 #endif
     }
 }

@@ -21,6 +21,7 @@ numpy.uint8 E8M0 scale per 32 elements along K; weights are [out][in].
 from __future__ import annotations
 
 import dataclasses
+import functools
 import os
 from concurrent.futures import ThreadPoolExecutor
 
@@ -42,6 +43,7 @@ class LayerConfig:
     seed: int = 0
     w_std: float = 0.02    # std of router and expert weights
     x_std: float = 1.0     # std of the activations
+    mx_gen: str = "quantize"  # MXFP4 weights: "quantize" N(0, w_std) draws, or "sampled" (see make_weights)
 
     @property
     def P(self) -> int:
@@ -63,6 +65,12 @@ CONFIGS = {
     # 20b-shaped layer with MXFP4 expert weights: decode and prefill
     "20b_mxfp4_decode": LayerConfig("20b_mxfp4_decode", T=16, H=2880, E=32, k=4, I=2880, wfmt=1),
     "20b_mxfp4_prefill": LayerConfig("20b_mxfp4_prefill", T=32768, H=2880, E=32, k=4, I=2880, wfmt=1),
+    # 120b-shaped layer with MXFP4 expert weights (the 120b model's experts are
+    # MXFP4 too), swept over SWEEP_120B; codes and scales sampled with the
+    # frequencies of quantised N(0, 0.02) draws (4x the 20b tensors: drawing and
+    # quantising that many normals on the host would take minutes)
+    "120b_mxfp4_sweep": LayerConfig("120b_mxfp4_sweep", T=32, H=2880, E=128, k=4, I=2880, wfmt=1,
+                                    mx_gen="sampled"),
 }
 SWEEP_120B = (1, 4, 8, 12, 16, 32)
 
@@ -195,9 +203,40 @@ def _workers() -> int:
     return max(1, min(16, os.cpu_count() or 1))
 
 
+@functools.lru_cache(maxsize=4)
+def _mx_sample_tables(std: float):
+    """256-entry lookup tables that turn a uniform random byte into an E2M1
+    code, or into an E8M0 scale byte, with the frequencies that
+    mxfp4_quantize gives N(0, std^2) data (measured once on a seeded sample of
+    512 x 2880 draws)."""
+    a = _rng(0x4D58, 0).standard_normal((512, 2880), dtype=np.float32) * np.float32(std)
+    packed, scales = mxfp4_quantize(a)
+    codes = np.concatenate([packed & 15, packed >> 4]).ravel()
+
+    def table(values):
+        vals, counts = np.unique(values, return_counts=True)
+        cdf = np.cumsum(counts) / counts.sum()
+        return vals[np.minimum(np.searchsorted(cdf, (np.arange(256) + 0.5) / 256), len(vals) - 1)].astype(np.uint8)
+
+    return table(codes), table(scales.ravel())
+
+
+def _mx_sampled(rng: np.random.Generator, rows: int, cols: int, std: float):
+    """MXFP4 bytes [rows][cols/2] and scales [rows][cols/32] whose codes and
+    scale bytes are drawn independently with the frequencies of quantised
+    N(0, std^2) data."""
+    ctab, stab = _mx_sample_tables(std)
+    c = ctab[rng.integers(0, 256, size=(rows, cols), dtype=np.uint8)]
+    packed = (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
+    scales = stab[rng.integers(0, 256, size=(rows, cols // 32), dtype=np.uint8)]
+    return np.ascontiguousarray(packed), np.ascontiguousarray(scales)
+
+
 def make_weights(cfg: LayerConfig) -> Weights:
     """Expert weights ~N(0, w_std^2): bf16, or MXFP4 quantized from the same
-    float draws.  One random stream per (tensor, expert)."""
+    float draws.  One random stream per (tensor, expert).  With mx_gen =
+    "sampled" the MXFP4 codes and scales are drawn directly from the
+    frequencies quantised N(0, w_std^2) data has (_mx_sampled)."""
     E, H, I = cfg.E, cfg.H, cfg.I
     if cfg.wfmt == 0:
         gu = np.empty((E, 2 * I, H), np.uint16)
@@ -217,6 +256,10 @@ def make_weights(cfg: LayerConfig) -> Weights:
     dns = np.empty((E, H, I // 32), np.uint8)
 
     def oneq(e):
+        if cfg.mx_gen == "sampled":
+            gu[e], gus[e] = _mx_sampled(_rng(cfg.seed, _WGU, e), 2 * I, H, cfg.w_std)
+            dn[e], dns[e] = _mx_sampled(_rng(cfg.seed, _WD, e), H, I, cfg.w_std)
+            return
         a = _rng(cfg.seed, _WGU, e).standard_normal((2 * I, H), dtype=np.float32) * np.float32(cfg.w_std)
         gu[e], gus[e] = mxfp4_quantize(a)
         b = _rng(cfg.seed, _WD, e).standard_normal((H, I), dtype=np.float32) * np.float32(cfg.w_std)

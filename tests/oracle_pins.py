@@ -494,6 +494,47 @@ def pin_route_k_equals_E(o):
         _close(w[t], full[idx[t]], rtol=1e-13)
 
 
+def pin_route_nan_logits(o):
+    """Reading for non-finite inputs: a NaN logit ranks below every number
+    (as -infinity), ties still to the lower index.  A NaN in a token's row
+    makes all its logits NaN: experts 0..k-1 in order, NaN weights.  A NaN in
+    one expert's router row makes that expert's logit NaN for every token: it
+    is never selected while k < E, and it comes last when k = E.  Checked
+    against an independent k-pass argmax over numpy logits with NaN replaced
+    by -inf, and other tokens must be unaffected."""
+    x, wr, _ = _rand_layer(17, 12, 32, 8, 3, 32)
+    nan = np.uint16(0x7FC0)
+    xn = x.copy()
+    xn[4, 7] = nan
+    _, idx, w = o.route(xn, wr, 3)
+    assert list(idx[4]) == [0, 1, 2] and np.isnan(w[4]).all(), (idx[4], w[4])
+    _, idx0, w0 = o.route(x, wr, 3)
+    keep = np.arange(12) != 4
+    assert (idx[keep] == idx0[keep]).all() and np.array_equal(w[keep], w0[keep])
+    wrn = wr.copy()
+    wrn[1, 5] = nan
+    ref = _f64(x) @ _f64(wrn).T
+    ref = np.where(np.isnan(ref), -np.inf, ref)
+    def kpass(l, k):  # k passes over the remaining experts: largest value, lowest index on ties
+        left = list(range(len(l)))
+        out = []
+        for _ in range(k):
+            j = max(left, key=lambda e: (l[e], -e))
+            out.append(j)
+            left.remove(j)
+        return out
+
+    for k in (3, 8):
+        _, idx, w = o.route(x, wrn, k)
+        for t in range(12):
+            assert list(idx[t]) == kpass(ref[t], k), (k, t, idx[t])
+            assert np.isfinite(w[t]).all() and abs(w[t].sum() - 1.0) <= 1e-12
+        if k == 8:
+            assert (idx[:, -1] == 1).all() and (w[:, -1] == 0.0).all()
+        else:
+            assert not (idx == 1).any()
+
+
 # --------------------------------------------------------------------------- permute pins
 
 

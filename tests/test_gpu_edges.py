@@ -121,6 +121,48 @@ def test_route_many_tokens(shape):
     assert np.max(np.abs(g.topk_w.cpu().numpy() - w_ref)) <= 1e-5
 
 
+@pytest.mark.parametrize("T,E,wfmt", [(16, 32, 0), (16, 128, 0), (16, 32, 2), (8192, 32, 0), (2048, 128, 0)],
+                         ids=lambda v: str(v))
+def test_nan_logits(T, E, wfmt):
+    """Regression for non-finite inputs (every top-k path: per-token ranks for
+    E <= 64, arg-max rounds above, and the selection fused into the
+    matrix-core logits kernel from 1024 tokens).  A NaN in one token's x row
+    makes all its logits NaN: it must get experts 0..k-1 (NaN ranks as
+    -infinity, ties to the lower index) and a NaN output row; a NaN in expert
+    1's router row makes that expert's logit NaN for every token, so it is
+    never selected.  Every index stays in [0, E) and distinct, and every other
+    token matches the oracle."""
+    k, H, I = 4, 256, 128
+    layer = _layer(T, H, E, k, I, wfmt=min(wfmt, 1), seed=21)
+    x = layer.x.copy()
+    nan_tok = T // 3
+    x[nan_tok, 17] = 0x7FC0
+    wr = layer.w_router.copy()
+    wr[1, 5] = 0x7FC0
+    layer = synth.Layer(layer.cfg, x, wr, layer.weights)
+    print(f"[edge] NaN logits T={T} E={E} wfmt={wfmt}", flush=True)
+    orc = oracle.get()
+    _, idx_ref, w_ref = orc.route(x, wr, k)
+    g = GpuLayer(layer, packed=wfmt == 2)
+    g.forward()
+    torch.cuda.synchronize()
+    idx = g.topk_idx.cpu().numpy()
+    assert ((idx >= 0) & (idx < E)).all()
+    assert all(len(set(r)) == k for r in idx.tolist())
+    keep = np.arange(T) != nan_tok
+    assert list(idx[nan_tok]) == list(range(k)) and not (idx[keep] == 1).any()
+    assert np.array_equal(idx, idx_ref)
+    w = g.topk_w.cpu().numpy()
+    assert np.isnan(w[nan_tok]).all() and np.max(np.abs(w[keep] - w_ref[keep])) <= 1e-5
+    y = bf16_dev_to_f64(g.y)
+    assert np.isnan(y[nan_tok]).all()
+    tokens = synth.sample_tokens(T, 256, 5)
+    tokens = tokens[tokens != nan_tok]
+    y_ref, _, _ = orc.forward_tokens(x, wr, layer.weights, k, I, tokens)
+    e = rel_err(y[tokens], y_ref)
+    assert e <= TOL, e
+
+
 def test_empty_batch_is_noop():
     layer = _layer(4, 64, 4, 2, 64)
     g = GpuLayer(layer)

@@ -30,10 +30,13 @@ CHECK_TOKENS = 512
 
 # "+packed": the same MXFP4 layer with its weights reordered on the device by
 # moe_mxfp4_pack (MOE_WFMT_MXFP4_PACKED), against the oracle on the row-major
-# weights; "@1": one token (single-stream decode, few touched experts).
+# weights; "@1": one token (single-stream decode, few touched experts);
+# "120b_mxfp4_T<t>": the 120b shape with MXFP4 experts, as the decode sweep
+# times it (packed order).
 CASES = ["tiny", "20b_decode"] + [f"120b_T{t}" for t in synth.SWEEP_120B] + [
     "20b_prefill_zipf", "20b_mxfp4_decode", "20b_mxfp4_prefill", "20b_mxfp4_decode+packed",
-    "20b_mxfp4_prefill+packed", "20b_mxfp4_decode@1+packed"]
+    "20b_mxfp4_prefill+packed", "20b_mxfp4_decode@1+packed"] + [
+    f"120b_mxfp4_T{t}+packed" for t in synth.SWEEP_120B]
 
 
 @functools.lru_cache(maxsize=1)
@@ -51,6 +54,9 @@ def make_case(name: str) -> synth.Layer:
     if name.startswith("120b_T"):
         cfg = synth.CONFIGS["120b_sweep"].with_T(int(name[len("120b_T"):]))
         wkey = "120b_sweep"
+    elif name.startswith("120b_mxfp4_T"):
+        cfg = synth.CONFIGS["120b_mxfp4_sweep"].with_T(int(name[len("120b_mxfp4_T"):]))
+        wkey = "120b_mxfp4_sweep"
     else:
         cfg = synth.CONFIGS[name]
         wkey = "20b_mxfp4_decode" if cfg.wfmt == 1 else name
