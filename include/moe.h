@@ -185,6 +185,24 @@ int moe_combine(const moe_dims* dims, const void* y_sorted, const int32_t* pair_
 int moe_forward(const moe_dims* dims, const void* x, const void* w_router, const moe_expert_weights* weights, void* y,
                 int32_t* topk_idx_out, float* topk_w_out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* moe_forward without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  It allocates nothing: the intermediates live in a
+ * library-owned device array of MOE_NOALLOC_SCRATCH_BYTES (32 MiB), one per
+ * GPU, held from library load until the process ends.  Arguments, results and
+ * errors as moe_forward; in addition MOE_ERR_WORKSPACE when
+ * moe_workspace_size(dims) exceeds MOE_NOALLOC_SCRATCH_BYTES (for the
+ * 2880-wide layers with k = 4: up to about 700 tokens).  Nothing in the array
+ * needs clearing between calls (every call writes what it later reads).
+ * Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on one GPU (other streams, other threads) race and must be serialised by
+ * the caller.  The first call on a device looks up the array's address
+ * (hipGetSymbolAddress) with that device current; a failure there returns
+ * MOE_ERR_HIP. */
+#define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
+int moe_forward_noalloc(const moe_dims* dims, const void* x, const void* w_router, const moe_expert_weights* weights,
+                        void* y, int32_t* topk_idx_out, float* topk_w_out, void* stream);
+
 /* Backward of moe_forward (the training variant: full-parameter fine-tuning,
  * "kappa-20b-131k" model card; bf16 with fp32 accumulation and activations
  * recomputed during backprop, "Persona Kappa: training a 20B LLM on desktop

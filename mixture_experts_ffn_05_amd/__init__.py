@@ -23,8 +23,8 @@ MOE_PACK_GATE_UP, MOE_PACK_DOWN = 0, 1
 MOE_PATH_AUTO, MOE_PATH_SKINNY, MOE_PATH_TILED = 0, 1, 2
 
 EXPORTED = ("moe_workspace_size", "moe_route", "moe_permute", "moe_gate_up", "moe_down", "moe_grouped_ffn",
-            "moe_combine", "moe_forward", "moe_backward_workspace_size", "moe_backward", "moe_mxfp4_quantize",
-            "moe_mxfp4_fakequant", "moe_mxfp4_pack", "moe_strerror", "moe_last_error")
+            "moe_combine", "moe_forward", "moe_forward_noalloc", "moe_backward_workspace_size", "moe_backward",
+            "moe_mxfp4_quantize", "moe_mxfp4_fakequant", "moe_mxfp4_pack", "moe_strerror", "moe_last_error")
 
 
 class MoeLibraryMissing(RuntimeError):
@@ -73,6 +73,7 @@ def library(path: str | None = None):
         "moe_grouped_ffn": [D, V, V, V, W, V, V, SZ, V],
         "moe_combine": [D, V, V, V, V, V],
         "moe_forward": [D, V, V, W, V, V, V, V, SZ, V],
+        "moe_forward_noalloc": [D, V, V, W, V, V, V, V],
         "moe_backward_workspace_size": [D, ctypes.POINTER(SZ)],
         "moe_backward": [D, V, V, W, V, V, V, V, V, V, SZ, V],
         "moe_mxfp4_quantize": [ctypes.c_int64, ctypes.c_int32, V, V, V, V],
@@ -175,6 +176,15 @@ def moe_forward(d, x, w_router, weights: moe_expert_weights, y, topk_idx_out, to
                                                _stream(stream)))
 
 
+def moe_forward_noalloc(d, x, w_router, weights: moe_expert_weights, y, topk_idx_out, topk_w_out, stream=None):
+    _check("moe_forward_noalloc", library().moe_forward_noalloc(ctypes.byref(d), _ptr(x), _ptr(w_router),
+                                                               ctypes.byref(weights), _ptr(y), _ptr(topk_idx_out),
+                                                               _ptr(topk_w_out), _stream(stream)))
+
+
+MOE_NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
 def moe_backward_workspace_size(d: moe_dims) -> int:
     n = ctypes.c_size_t(0)
     _check("moe_backward_workspace_size", library().moe_backward_workspace_size(ctypes.byref(d), ctypes.byref(n)))
@@ -203,7 +213,8 @@ def moe_mxfp4_pack(d: moe_dims, which: int, w, scales, w_packed, scales_packed, 
 
 
 __all__ = ["library", "dims", "expert_weights", "strerror", "moe_workspace_size", "moe_route", "moe_permute",
-           "moe_gate_up", "moe_down", "moe_grouped_ffn", "moe_combine", "moe_forward", "moe_backward_workspace_size",
+           "moe_gate_up", "moe_down", "moe_grouped_ffn", "moe_combine", "moe_forward", "moe_forward_noalloc",
+           "MOE_NOALLOC_SCRATCH_BYTES", "moe_backward_workspace_size",
            "moe_backward", "moe_mxfp4_quantize",
            "moe_mxfp4_fakequant", "moe_mxfp4_pack", "moe_dims",
            "moe_expert_weights", "MoeError", "MoeLibraryMissing", "EXPORTED", "LIB_PATH"]

@@ -108,6 +108,12 @@ int hip_status(hipError_t e)
     return MOE_ERR_HIP;
 }
 
+}  // namespace
+
+void moe::set_last_error(const char* text) { g_last_error = text ? text : ""; }
+
+namespace {
+
 template <typename T>
 T* region(void* ws, size_t off)
 {

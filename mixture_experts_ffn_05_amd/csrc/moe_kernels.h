@@ -9,6 +9,9 @@
 
 namespace moe {
 
+// Text kept for moe_last_error() on the calling thread (C-ABI layer).
+void set_last_error(const char* text);
+
 // ------------------------------------------------------------------ route
 // Exact logits (fp64 accumulation of exact bf16 products), one wave per
 // (token, group of experts).  logits [T][E] fp64.
