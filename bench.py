@@ -142,25 +142,28 @@ def measured_traffic(kernel: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def device_layer(layer, packed: bool = False, weights_dev=None):
+PATHS = {"auto": 0, "skinny": 1, "tiled": 2, "tiled_dequant": 3, "tiled_mx": 4}
+
+
+def device_layer(layer, packed: bool = False, weights_dev=None, path: int = 0):
     """The package's DeviceLayer for a synthetic layer (synth.Layer)."""
     from mixture_experts_ffn_05_amd.layer import DeviceLayer
     c, w = layer.cfg, layer.weights
     host = {} if weights_dev is not None else dict(gate_up=w.gate_up, down=w.down, gate_up_scale=w.gate_up_scale,
                                                    down_scale=w.down_scale)
     return DeviceLayer(c.T, c.H, c.E, c.k, c.I, c.wfmt, layer.x, layer.w_router, packed=packed,
-                       weights_dev=weights_dev, **host)
+                       weights_dev=weights_dev, path=path, **host)
 
 
 class Timed:
     """One workload on the device, with rotated weight copies."""
 
-    def __init__(self, layer, n_copies: int, packed: bool = False, weights_dev=None):
+    def __init__(self, layer, n_copies: int, packed: bool = False, weights_dev=None, path: int = 0):
         import torch
 
         import mixture_experts_ffn_05_amd as moe
         self.torch, self.moe = torch, moe
-        self.g = device_layer(layer, packed=packed, weights_dev=weights_dev)
+        self.g = device_layer(layer, packed=packed, weights_dev=weights_dev, path=path)
         c = layer.cfg
         g = self.g
         self.copies = [(g.gate_up, g.down, g.gate_up_scale, g.down_scale)]
@@ -682,6 +685,8 @@ def main():
                     help="write a text summary of a rocprofv3 --kernel-trace --stats run")
     ap.add_argument("--traffic-kernel", default="gate_up_skinny", choices=sorted(TRAFFIC_RUNS),
                     help="which kernel --write-traffic summarises")
+    ap.add_argument("--path", default="auto", choices=sorted(PATHS),
+                    help="expert-FFN schedule for --only (auto, skinny, tiled, tiled_dequant, tiled_mx)")
     ap.add_argument("--only", metavar="WORKLOAD",
                     help="time just this synthetic workload (e.g. 20b_prefill_zipf) for --steps layer steps and "
                          "print its line; for profiling one regime")
@@ -729,13 +734,17 @@ def main():
                               "touched_experts": touched, "hbm_frac": round(total_b / sec / 1e9 / HBM_PEAK_GBS, 4),
                               "stages_us": {k: round(v, 1) for k, v in stages.items()}}))
             return
-        tm = Timed(layer, 1, packed)
+        tm = Timed(layer, 1, packed, path=PATHS[args.path])
         sec = tm.run(args.steps, args.warmup)
-        fl, _ = layer_flops(layer.cfg)
-        print(json.dumps({"workload": args.only, "tokens": layer.cfg.T, "steps": args.steps,
+        stages = tm.stages(args.steps, 1)
+        fl, fl_gu = layer_flops(layer.cfg)
+        print(json.dumps({"workload": args.only, "path": args.path, "tokens": layer.cfg.T, "steps": args.steps,
                           "us_per_layer": round(sec * 1e6, 1), "tokens_per_s": round(layer.cfg.T / sec, 1),
                           "tflops": round(fl / sec / 1e12, 2),
-                          "mfma_bf16_frac": round(fl / sec / 1e12 / BF16_PEAK_TFLOPS, 4)}))
+                          "mfma_bf16_frac": round(fl / sec / 1e12 / BF16_PEAK_TFLOPS, 4),
+                          "mfma_fp4_frac": round(fl / sec / 1e12 / FP4_PEAK_TFLOPS, 4),
+                          "gate_up_tflops": round(fl_gu / (stages["gate_up"] * 1e-6) / 1e12, 2),
+                          "stages_us": {k: round(v, 1) for k, v in stages.items()}}))
         return
 
     layer = synth.make_layer("20b_decode")

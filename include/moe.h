@@ -117,8 +117,31 @@ enum { MOE_WFMT_BF16 = 0, MOE_WFMT_MXFP4 = 1, MOE_WFMT_MXFP4_PACKED = 2 };
 
 /* Expert-FFN schedule.  AUTO picks SKINNY when tokens per expert are few
  * (weight streaming at HBM rate) and TILED otherwise (LDS-tiled grouped GEMM).
- * Both compute the same function; forcing one is for testing and tuning. */
-enum { MOE_PATH_AUTO = 0, MOE_PATH_SKINNY = 1, MOE_PATH_TILED = 2 };
+ * For MXFP4 weights the tiled regime has two kernels:
+ *   TILED_DEQUANT  E2M1 x E8M0 decoded exactly to bf16 while staged into LDS,
+ *                  bf16 MFMA (W4A16 as the pages describe it: "Persona Kappa:
+ *                  training a 20B LLM on desktop GPUs", section
+ *                  "Quantization-Aware Training (QAT)");
+ *   TILED_MX       the weights fed as stored to the MX matrix cores
+ *                  (v_mfma_scale_f32_32x32x64_f8f6f4), the bf16 activations
+ *                  split per 32-value block into two MXFP6 (E2M3) terms,
+ *                  x ~ hi + lo (see moe_mx_split); needs H and I multiples
+ *                  of 64, else MOE_ERR_UNSUPPORTED.  Its rounding differs
+ *                  from the bf16 path's (hi + lo keeps about as much of each
+ *                  activation as bf16 does; both stay within the layer's
+ *                  1e-2 * max|y| tolerance), so the two give different bits.
+ * TILED (and AUTO in the tiled regime) takes TILED_DEQUANT, the faster of the
+ * two on the 20b prefill shapes; TILED_MX runs only when asked for.  For bf16
+ * weights all tiled paths are the bf16 kernel except TILED_MX, which returns
+ * MOE_ERR_UNSUPPORTED.  Every path computes the same function; forcing one is
+ * for testing and tuning. */
+enum {
+    MOE_PATH_AUTO = 0,
+    MOE_PATH_SKINNY = 1,
+    MOE_PATH_TILED = 2,
+    MOE_PATH_TILED_DEQUANT = 3,
+    MOE_PATH_TILED_MX = 4
+};
 
 typedef struct moe_dims {
     int32_t T, H, E, k, I;
@@ -291,6 +314,26 @@ int moe_mxfp4_fakequant(int64_t rows, int32_t cols, const void* w, void* out, vo
 enum { MOE_PACK_GATE_UP = 0, MOE_PACK_DOWN = 1 };
 int moe_mxfp4_pack(const moe_dims* dims, int32_t which, const uint8_t* w, const uint8_t* scales, uint8_t* w_packed,
                    uint8_t* scales_packed, void* stream);
+
+/* The activation split of the MX path (MOE_PATH_TILED_MX): bf16 x [rows][cols]
+ * (cols % 32 == 0) as two MXFP6 terms per block of 32 consecutive elements of
+ * a row.  With amax the block's largest |x| and
+ *   S  = clamp(floor(log2 amax) - 2 + 127, 1, 254)   (OCP Microscaling v1.0
+ *        shared exponent for E2M3, whose largest exponent is 2),
+ *   hi = each x / 2^(S-127) rounded to the nearest E2M3 value (ties to the
+ *        even code, saturating at +-7.5), times 2^(S-127),
+ *   lo = x - hi (exact), encoded the same way with its own S2 from its amax,
+ * it writes codes u8 [rows][cols/32][48]: the block's 32 hi codes (6 bits
+ * each, element j at bits 6j..6j+5 of the 24 bytes, little-endian), then its
+ * 32 lo codes; and scales u8 [rows][cols/32][2]: S, then S2.  E2M3 codes:
+ * sign bit 5, exponent bits 4:3 (bias 1), mantissa bits 2:0.  The layer's MX
+ * path makes these itself in its workspace; this entry point is for callers
+ * and tests.  Errors: rows < 0 or a null pointer -> MOE_ERR_INVALID_ARG;
+ * cols % 32 != 0 or cols <= 0 -> MOE_ERR_UNSUPPORTED; x or codes not 16-byte
+ * aligned, scales not 2-byte aligned -> MOE_ERR_MISALIGNED.  rows = 0 returns
+ * MOE_OK.  Inputs are finite; a NaN or Inf element gives undefined codes for
+ * its block.  Asynchronous on `stream` like every call. */
+int moe_mx_split(int64_t rows, int32_t cols, const void* x, uint8_t* codes, uint8_t* scales, void* stream);
 
 /* Static text for an error code. */
 const char* moe_strerror(int code);

@@ -20,11 +20,12 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_MISALIGNED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(6)
 MOE_WFMT_BF16, MOE_WFMT_MXFP4, MOE_WFMT_MXFP4_PACKED = 0, 1, 2
 MOE_PACK_GATE_UP, MOE_PACK_DOWN = 0, 1
-MOE_PATH_AUTO, MOE_PATH_SKINNY, MOE_PATH_TILED = 0, 1, 2
+MOE_PATH_AUTO, MOE_PATH_SKINNY, MOE_PATH_TILED, MOE_PATH_TILED_DEQUANT, MOE_PATH_TILED_MX = 0, 1, 2, 3, 4
 
 EXPORTED = ("moe_workspace_size", "moe_route", "moe_permute", "moe_gate_up", "moe_down", "moe_grouped_ffn",
             "moe_combine", "moe_forward", "moe_forward_noalloc", "moe_backward_workspace_size", "moe_backward",
-            "moe_mxfp4_quantize", "moe_mxfp4_fakequant", "moe_mxfp4_pack", "moe_strerror", "moe_last_error")
+            "moe_mxfp4_quantize", "moe_mxfp4_fakequant", "moe_mxfp4_pack", "moe_mx_split", "moe_strerror",
+            "moe_last_error")
 
 
 class MoeLibraryMissing(RuntimeError):
@@ -79,6 +80,7 @@ def library(path: str | None = None):
         "moe_mxfp4_quantize": [ctypes.c_int64, ctypes.c_int32, V, V, V, V],
         "moe_mxfp4_fakequant": [ctypes.c_int64, ctypes.c_int32, V, V, V],
         "moe_mxfp4_pack": [D, ctypes.c_int32, V, V, V, V, V],
+        "moe_mx_split": [ctypes.c_int64, ctypes.c_int32, V, V, V, V],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -212,9 +214,13 @@ def moe_mxfp4_pack(d: moe_dims, which: int, w, scales, w_packed, scales_packed, 
                                                      _ptr(scales_packed), _stream(stream)))
 
 
+def moe_mx_split(rows: int, cols: int, x, codes, scales, stream=None):
+    _check("moe_mx_split", library().moe_mx_split(rows, cols, _ptr(x), _ptr(codes), _ptr(scales), _stream(stream)))
+
+
 __all__ = ["library", "dims", "expert_weights", "strerror", "moe_workspace_size", "moe_route", "moe_permute",
            "moe_gate_up", "moe_down", "moe_grouped_ffn", "moe_combine", "moe_forward", "moe_forward_noalloc",
            "MOE_NOALLOC_SCRATCH_BYTES", "moe_backward_workspace_size",
            "moe_backward", "moe_mxfp4_quantize",
-           "moe_mxfp4_fakequant", "moe_mxfp4_pack", "moe_dims",
+           "moe_mxfp4_fakequant", "moe_mxfp4_pack", "moe_mx_split", "moe_dims",
            "moe_expert_weights", "MoeError", "MoeLibraryMissing", "EXPORTED", "LIB_PATH"]

@@ -20,8 +20,20 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 // point uses this one layout, so one workspace of moe_workspace_size() bytes
 // serves all of them.
 struct Layout {
-    size_t topk_idx, topk_w, logits, offsets, sorted, rank, perm_scratch, h, y_sorted, total;
+    size_t topk_idx, topk_w, logits, offsets, sorted, rank, perm_scratch, h, y_sorted;
+    size_t xs_codes, xs_scales, hs_codes, hs_scales;  // MX path: split x and h (0 bytes when unused)
+    size_t total;
 };
+
+// The MX path applies: MXFP4 weights, H and I multiples of 64, and split
+// activations small enough for the kernel's 32-bit byte offsets.
+bool mx_fits(const moe_dims& d)
+{
+    if (d.wfmt == MOE_WFMT_BF16 || !moe::mx_supported(d.H, d.I)) return false;
+    const uint64_t lim = 1ull << 31;
+    const uint64_t P = (uint64_t)d.T * (uint64_t)d.k;
+    return (uint64_t)d.T * d.H / 32 * 48 < lim && P * d.I / 32 * 48 < lim;
+}
 
 Layout layout_for(const moe_dims& d)
 {
@@ -42,6 +54,11 @@ Layout layout_for(const moe_dims& d)
     L.perm_scratch = take(moe::permute_scratch_bytes((int64_t)P, d.E));
     L.h = take(P * (size_t)d.I * 2);
     L.y_sorted = take(P * (size_t)d.H * 2);
+    const bool mx = mx_fits(d);
+    L.xs_codes = take(mx ? T * (size_t)d.H / 32 * 48 : 0);
+    L.xs_scales = take(mx ? T * (size_t)d.H / 32 * 2 : 0);
+    L.hs_codes = take(mx ? P * (size_t)d.I / 32 * 48 : 0);
+    L.hs_scales = take(mx ? P * (size_t)d.I / 32 * 2 : 0);
     L.total = at;
     return L;
 }
@@ -68,8 +85,8 @@ int check_dims(const moe_dims* d)
     if (d->H % 32 != 0 || d->I % 32 != 0) return MOE_ERR_UNSUPPORTED;
     if (d->wfmt != MOE_WFMT_BF16 && d->wfmt != MOE_WFMT_MXFP4 && d->wfmt != MOE_WFMT_MXFP4_PACKED)
         return MOE_ERR_UNSUPPORTED;
-    if (d->path != MOE_PATH_AUTO && d->path != MOE_PATH_SKINNY && d->path != MOE_PATH_TILED)
-        return MOE_ERR_UNSUPPORTED;
+    if (d->path < MOE_PATH_AUTO || d->path > MOE_PATH_TILED_MX) return MOE_ERR_UNSUPPORTED;
+    if (d->path == MOE_PATH_TILED_MX && !mx_fits(*d)) return MOE_ERR_UNSUPPORTED;
     if (d->wfmt == MOE_WFMT_MXFP4_PACKED && d->path == MOE_PATH_SKINNY && !packed_skinny_fits(*d))
         return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
@@ -128,9 +145,14 @@ constexpr int kSkinnyMaxT = 64;
 bool use_skinny(const moe_dims& d)
 {
     if (d.path == MOE_PATH_SKINNY) return true;
-    if (d.path == MOE_PATH_TILED) return false;
+    if (d.path != MOE_PATH_AUTO) return false;
     return d.T <= kSkinnyMaxT && (d.wfmt != MOE_WFMT_MXFP4_PACKED || packed_skinny_fits(d));
 }
+
+// Tiled regime on the MX matrix cores (MXFP4 weights; see MOE_PATH_TILED_MX):
+// only when asked for, since on the 20b prefill shapes the bf16-decode kernel
+// is still the faster one.
+bool use_mx(const moe_dims& d) { return d.path == MOE_PATH_TILED_MX && mx_fits(d); }
 
 moe::FfnArgs ffn_args(const moe_dims& d)
 {
@@ -181,8 +203,10 @@ int do_permute(const moe_dims& d, const int32_t* idx, int32_t* off, int32_t* sp,
     return hip_status(moe::launch_permute(d.T * d.k, d.E, idx, off, sp, pr, region<void>(ws, L.perm_scratch), s));
 }
 
+// The MX path splits the activations into the workspace first (x: T rows,
+// h: P rows), then runs the MX grouped GEMM on them.
 int do_gate_up(const moe_dims& d, const void* x, const int32_t* off, const int32_t* sp, const moe_expert_weights& w,
-               void* h, hipStream_t s)
+               void* h, void* ws, hipStream_t s)
 {
     moe::FfnArgs a = ffn_args(d);
     a.x = static_cast<const uint16_t*>(x);
@@ -191,10 +215,20 @@ int do_gate_up(const moe_dims& d, const void* x, const int32_t* off, const int32
     a.w = w.gate_up;
     a.w_scale = w.gate_up_scale;
     a.out = static_cast<uint16_t*>(h);
+    if (use_mx(d)) {
+        const Layout L = layout_for(d);
+        a.a_codes = region<uint8_t>(ws, L.xs_codes);
+        a.a_scales = region<uint8_t>(ws, L.xs_scales);
+        int rc = hip_status(moe::launch_mx_split(a.x, d.T, d.H, region<uint8_t>(ws, L.xs_codes),
+                                                 region<uint8_t>(ws, L.xs_scales), s));
+        if (rc) return rc;
+        return hip_status(moe::launch_gate_up_mx(a, s));
+    }
     return hip_status(use_skinny(d) ? moe::launch_gate_up_skinny(a, s) : moe::launch_gate_up_tiled(a, s));
 }
 
-int do_down(const moe_dims& d, const void* h, const int32_t* off, const moe_expert_weights& w, void* ys, hipStream_t s)
+int do_down(const moe_dims& d, const void* h, const int32_t* off, const moe_expert_weights& w, void* ys, void* ws,
+            hipStream_t s)
 {
     moe::FfnArgs a = ffn_args(d);
     a.offsets = off;
@@ -202,6 +236,15 @@ int do_down(const moe_dims& d, const void* h, const int32_t* off, const moe_expe
     a.w = w.down;
     a.w_scale = w.down_scale;
     a.out = static_cast<uint16_t*>(ys);
+    if (use_mx(d)) {
+        const Layout L = layout_for(d);
+        a.a_codes = region<uint8_t>(ws, L.hs_codes);
+        a.a_scales = region<uint8_t>(ws, L.hs_scales);
+        int rc = hip_status(moe::launch_mx_split(a.a_rows, (int64_t)d.T * d.k, d.I, region<uint8_t>(ws, L.hs_codes),
+                                                 region<uint8_t>(ws, L.hs_scales), s));
+        if (rc) return rc;
+        return hip_status(moe::launch_down_mx(a, s));
+    }
     return hip_status(use_skinny(d) ? moe::launch_down_skinny(a, s) : moe::launch_down_tiled(a, s));
 }
 
@@ -406,9 +449,8 @@ int moe_gate_up(const moe_dims* dims, const void* x, const int32_t* expert_offse
     if ((rc = check_ptr(x, 16)) || (rc = check_ptr(expert_offsets, 4)) || (rc = check_ptr(sorted_pairs, 4)) ||
         (rc = check_weights(d, weights)) || (rc = check_ptr(h, 16)))
         return rc;
-    (void)workspace;
-    (void)workspace_bytes;
-    return do_gate_up(d, x, expert_offsets, sorted_pairs, *weights, h, static_cast<hipStream_t>(stream));
+    if (use_mx(d) && (rc = check_ws(d, workspace, workspace_bytes))) return rc;
+    return do_gate_up(d, x, expert_offsets, sorted_pairs, *weights, h, workspace, static_cast<hipStream_t>(stream));
 }
 
 int moe_down(const moe_dims* dims, const void* h, const int32_t* expert_offsets, const moe_expert_weights* weights,
@@ -421,9 +463,8 @@ int moe_down(const moe_dims* dims, const void* h, const int32_t* expert_offsets,
     if ((rc = check_ptr(h, 16)) || (rc = check_ptr(expert_offsets, 4)) || (rc = check_weights(d, weights)) ||
         (rc = check_ptr(y_sorted, 16)))
         return rc;
-    (void)workspace;
-    (void)workspace_bytes;
-    return do_down(d, h, expert_offsets, *weights, y_sorted, static_cast<hipStream_t>(stream));
+    if (use_mx(d) && (rc = check_ws(d, workspace, workspace_bytes))) return rc;
+    return do_down(d, h, expert_offsets, *weights, y_sorted, workspace, static_cast<hipStream_t>(stream));
 }
 
 int moe_grouped_ffn(const moe_dims* dims, const void* x, const int32_t* expert_offsets, const int32_t* sorted_pairs,
@@ -440,8 +481,8 @@ int moe_grouped_ffn(const moe_dims* dims, const void* x, const int32_t* expert_o
         return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
     void* h = region<void>(workspace, layout_for(d).h);
-    if ((rc = do_gate_up(d, x, expert_offsets, sorted_pairs, *weights, h, s))) return rc;
-    return do_down(d, h, expert_offsets, *weights, y_sorted, s);
+    if ((rc = do_gate_up(d, x, expert_offsets, sorted_pairs, *weights, h, workspace, s))) return rc;
+    return do_down(d, h, expert_offsets, *weights, y_sorted, workspace, s);
 }
 
 int moe_combine(const moe_dims* dims, const void* y_sorted, const int32_t* pair_rank, const float* topk_w, void* y,
@@ -480,8 +521,8 @@ int moe_forward(const moe_dims* dims, const void* x, const void* w_router, const
     void* h = region<void>(workspace, L.h);
     void* ys = region<void>(workspace, L.y_sorted);
     if ((rc = do_route_permute(d, x, w_router, idx, w, off, sp, pr, workspace, s))) return rc;
-    if ((rc = do_gate_up(d, x, off, sp, *weights, h, s))) return rc;
-    if ((rc = do_down(d, h, off, *weights, ys, s))) return rc;
+    if ((rc = do_gate_up(d, x, off, sp, *weights, h, workspace, s))) return rc;
+    if ((rc = do_down(d, h, off, *weights, ys, workspace, s))) return rc;
     return hip_status(moe::launch_combine(d.T, d.H, d.k, static_cast<const uint16_t*>(ys), pr, w,
                                           static_cast<uint16_t*>(y), s));
 }
@@ -533,6 +574,17 @@ int moe_mxfp4_pack(const moe_dims* dims, int32_t which, const uint8_t* w, const 
         return MOE_ERR_INVALID_ARG;
     return hip_status(moe::launch_mxfp4_pack(gu, dims->E, dims->I, dims->H, w, scales, w_packed, scales_packed,
                                              static_cast<hipStream_t>(stream)));
+}
+
+int moe_mx_split(int64_t rows, int32_t cols, const void* x, uint8_t* codes, uint8_t* scales, void* stream)
+{
+    if (rows < 0) return MOE_ERR_INVALID_ARG;
+    if (cols <= 0 || cols % 32 != 0) return MOE_ERR_UNSUPPORTED;
+    if (rows == 0) return MOE_OK;
+    int rc;
+    if ((rc = check_ptr(x, 16)) || (rc = check_ptr(codes, 16)) || (rc = check_ptr(scales, 2))) return rc;
+    return hip_status(moe::launch_mx_split(static_cast<const uint16_t*>(x), rows, cols, codes, scales,
+                                           static_cast<hipStream_t>(stream)));
 }
 
 int moe_mxfp4_fakequant(int64_t rows, int32_t cols, const void* w, void* out, void* stream)

@@ -49,6 +49,11 @@ struct FfnArgs {
     const void* w;              // gate_up or down
     const uint8_t* w_scale;     // MXFP4 scales or null
     const uint16_t* a_rows;     // down: h [P][I] (sorted rows)
+    // MX path: the activations split into two MXFP6 terms (launch_mx_split):
+    // codes [rows][K/32][48] and scales [rows][K/32][2]; rows are tokens
+    // (gate/up, gathered through sorted_pairs) or sorted pairs (down)
+    const uint8_t* a_codes;
+    const uint8_t* a_scales;
     uint16_t* out;              // gate/up: h [P][I]; down: y_sorted [P][H]
     uint16_t* gu_out;           // tiled gate/up only, optional: g then u [P][2I] (bf16), for the backward
     // weight-gradient mode of the tiled kernel: C[e][m][n] = sum_j A_e[m][j] B_e[n][j]
@@ -66,6 +71,18 @@ bool skinny4_supported(const FfnArgs& a);
 hipError_t launch_down_skinny(const FfnArgs& a, hipStream_t s);
 hipError_t launch_gate_up_tiled(const FfnArgs& a, hipStream_t s);
 hipError_t launch_down_tiled(const FfnArgs& a, hipStream_t s);
+
+// MX path (MXFP4 weights on the MX matrix cores).  The activations are first
+// split into two MXFP6 (E2M3) terms per 32-element block, x ~ hi + lo:
+// in bf16 [rows][K] -> codes [rows][K/32][48] (hi 24 B, then lo 24 B, 6 bits
+// per element) + scales [rows][K/32][2] (E8M0 of hi, of lo).  K % 32 == 0.
+hipError_t launch_mx_split(const uint16_t* in, int64_t rows, int K, uint8_t* codes, uint8_t* scales, hipStream_t s);
+// Grouped GEMMs on v_mfma_scale_f32_32x32x64_f8f6f4 (weights E2M1, activations
+// the two E2M3 terms), same outputs as launch_gate_up_tiled / launch_down_tiled;
+// a.a_codes / a.a_scales hold the split activations.  Needs K % 64 == 0.
+bool mx_supported(int H, int I);
+hipError_t launch_gate_up_mx(const FfnArgs& a, hipStream_t s);
+hipError_t launch_down_mx(const FfnArgs& a, hipStream_t s);
 
 // ------------------------------------------------------------------ combine
 hipError_t launch_combine(int T, int H, int k, const uint16_t* y_sorted, const int32_t* pair_rank,

@@ -38,9 +38,12 @@ int main(void)
 {
     const int T = 16, H = 256, E = 8, k = 2, I = 128, P = T * k;
     moe_dims d = {T, H, E, k, I, MOE_WFMT_BF16, MOE_PATH_AUTO};
-    size_t ws_bytes = 0;
+    size_t ws_bytes = 0, ws_mx = 0;
     EXPECT(moe_workspace_size(&d, &ws_bytes), MOE_OK, 0);
-    char* ws = buf(ws_bytes);
+    moe_dims dmx = d; dmx.wfmt = MOE_WFMT_MXFP4;
+    EXPECT(moe_workspace_size(&dmx, &ws_mx), MOE_OK, 0);
+    if (ws_mx <= ws_bytes) { fprintf(stderr, "the MX path's split activations add no workspace\n"); ++failures; }
+    char* ws = buf(ws_mx);
     char* x = buf((size_t)T * H * 2);
     char* wr = buf((size_t)E * H * 2);
     char* gu = buf((size_t)E * 2 * I * H * 2);
@@ -79,8 +82,29 @@ int main(void)
             moe_dims dd = d;
             dd.path = path;
             dd.wfmt = fmt;
-            EXPECT(moe_forward(&dd, x, wr, fmt ? &WM : &W, y, idx, w, ws, ws_bytes, NULL), MOE_OK, 1);
+            EXPECT(moe_forward(&dd, x, wr, fmt ? &WM : &W, y, idx, w, ws, fmt ? ws_mx : ws_bytes, NULL), MOE_OK, 1);
         }
+    /* the MX tiled path: MXFP4 only, H and I multiples of 64, its workspace */
+    dmx.path = MOE_PATH_TILED_MX;
+    EXPECT(moe_forward(&dmx, x, wr, &WM, y, NULL, NULL, ws, ws_mx, NULL), MOE_OK, 1);
+    EXPECT(moe_forward(&dmx, x, wr, &WM, y, NULL, NULL, ws, ws_bytes, NULL), MOE_ERR_WORKSPACE, 0);
+    EXPECT(moe_gate_up(&dmx, x, off, sp, &WM, h, ws, ws_bytes, NULL), MOE_ERR_WORKSPACE, 0);
+    EXPECT(moe_gate_up(&dmx, x, off, sp, &WM, h, ws, ws_mx, NULL), MOE_OK, 1);
+    EXPECT(moe_down(&dmx, h, off, &WM, ys, ws, ws_mx, NULL), MOE_OK, 1);
+    moe_dims dbad = dmx; dbad.wfmt = MOE_WFMT_BF16;
+    EXPECT(moe_workspace_size(&dbad, &n), MOE_ERR_UNSUPPORTED, 0);
+    dbad = dmx; dbad.H = 96;
+    EXPECT(moe_workspace_size(&dbad, &n), MOE_ERR_UNSUPPORTED, 0);
+    dbad = dmx; dbad.path = 5;
+    EXPECT(moe_workspace_size(&dbad, &n), MOE_ERR_UNSUPPORTED, 0);
+    dbad = dmx; dbad.path = MOE_PATH_TILED_DEQUANT;
+    EXPECT(moe_forward(&dbad, x, wr, &WM, y, NULL, NULL, ws, ws_mx, NULL), MOE_OK, 1);
+    EXPECT(moe_mx_split(T, H, x, (uint8_t*)ys, sgu, NULL), MOE_OK, 1);
+    EXPECT(moe_mx_split(T, 48, x, (uint8_t*)ys, sgu, NULL), MOE_ERR_UNSUPPORTED, 0);
+    EXPECT(moe_mx_split(-1, H, x, (uint8_t*)ys, sgu, NULL), MOE_ERR_INVALID_ARG, 0);
+    EXPECT(moe_mx_split(T, H, x, (uint8_t*)ys + 8, sgu, NULL), MOE_ERR_MISALIGNED, 0);
+    EXPECT(moe_mx_split(T, H, x, (uint8_t*)ys, sgu + 1, NULL), MOE_ERR_MISALIGNED, 0);
+    EXPECT(moe_mx_split(0, H, NULL, NULL, NULL, NULL), MOE_OK, 0);
     EXPECT(moe_forward(&d, x, wr, &W, y, NULL, NULL, ws, ws_bytes, NULL), MOE_OK, 1);
     EXPECT(moe_forward(&d, NULL, wr, &W, y, NULL, NULL, ws, ws_bytes, NULL), MOE_ERR_INVALID_ARG, 0);
     EXPECT(moe_forward(&d, x + 2, wr, &W, y, NULL, NULL, ws, ws_bytes, NULL), MOE_ERR_MISALIGNED, 0);
@@ -88,10 +112,10 @@ int main(void)
     EXPECT(moe_forward(&d, x, wr, &W, y, idx, (float*)((char*)w + 2), ws, ws_bytes, NULL), MOE_ERR_MISALIGNED, 0);
     EXPECT(moe_forward(&d, x, wr, NULL, y, NULL, NULL, ws, ws_bytes, NULL), MOE_ERR_INVALID_ARG, 0);
     moe_dims dm = d; dm.wfmt = MOE_WFMT_MXFP4;
-    EXPECT(moe_forward(&dm, x, wr, &W, y, NULL, NULL, ws, ws_bytes, NULL), MOE_ERR_INVALID_ARG, 0);
+    EXPECT(moe_forward(&dm, x, wr, &W, y, NULL, NULL, ws, ws_mx, NULL), MOE_ERR_INVALID_ARG, 0);
     dm.wfmt = MOE_WFMT_MXFP4_PACKED;
     moe_expert_weights WP = {gu, sgu + 1, dn, sdn};
-    EXPECT(moe_forward(&dm, x, wr, &WP, y, NULL, NULL, ws, ws_bytes, NULL), MOE_ERR_MISALIGNED, 0);
+    EXPECT(moe_forward(&dm, x, wr, &WP, y, NULL, NULL, ws, ws_mx, NULL), MOE_ERR_MISALIGNED, 0);
     moe_dims d0 = d; d0.T = 0;
     EXPECT(moe_forward(&d0, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 0, NULL), MOE_OK, 0);
 

@@ -34,6 +34,10 @@ bool skinny4_supported(const FfnArgs& a)
 hipError_t launch_down_skinny(const FfnArgs&, hipStream_t) { return count(); }
 hipError_t launch_gate_up_tiled(const FfnArgs&, hipStream_t) { return count(); }
 hipError_t launch_down_tiled(const FfnArgs&, hipStream_t) { return count(); }
+hipError_t launch_mx_split(const uint16_t*, int64_t, int, uint8_t*, uint8_t*, hipStream_t) { return count(); }
+bool mx_supported(int H, int I) { return H % 64 == 0 && I % 64 == 0; }
+hipError_t launch_gate_up_mx(const FfnArgs&, hipStream_t) { return count(); }
+hipError_t launch_down_mx(const FfnArgs&, hipStream_t) { return count(); }
 hipError_t launch_combine(int, int, int, const uint16_t*, const int32_t*, const float*, uint16_t*, hipStream_t) { return count(); }
 int backward_pad_rows(int P, int E) { return P + 64 * E; }
 hipError_t launch_zero_f32(float*, long long, hipStream_t) { return count(); }

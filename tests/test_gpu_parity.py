@@ -6,8 +6,9 @@ max|gpu - ref| <= 1e-2 * max|ref| (fp32 accumulation, bf16 storage).  Configs
 with more than 512 tokens are checked on a seeded sample of 512 tokens (each
 token's output depends on that token alone); routing and permutation are
 still checked on all tokens.  Both expert-FFN schedules (skinny and tiled)
-are forced on every config; the MXFP4 configs also run with the weights in
-the packed order.
+are forced on every config, and for MXFP4 weights both tiled kernels (MX
+matrix cores, and bf16 decode); the MXFP4 configs also run with the weights
+in the packed order.
 """
 from __future__ import annotations
 
@@ -122,9 +123,20 @@ def test_permute(case):
     assert np.array_equal(g.pair_rank.cpu().numpy(), case.pr)
 
 
-@pytest.mark.parametrize("path", [moe.MOE_PATH_SKINNY, moe.MOE_PATH_TILED], ids=["skinny", "tiled"])
+# For MXFP4 weights TILED_MX runs the MX-core kernel and TILED the bf16-decode
+# one; for bf16 weights TILED is the only tiled kernel.
+STAGE_PATHS = [moe.MOE_PATH_SKINNY, moe.MOE_PATH_TILED, moe.MOE_PATH_TILED_MX]
+
+
+def _skip_duplicate(case, path):
+    if path == moe.MOE_PATH_TILED_MX and case.cfg.wfmt == 0:
+        pytest.skip("bf16 weights have no MX-core path")
+
+
+@pytest.mark.parametrize("path", STAGE_PATHS, ids=["skinny", "tiled", "tiled_mx"])
 def test_expert_stages(case, path):
     """gate/up+SwiGLU -> h, down -> y_sorted, combine -> y, each against the oracle."""
+    _skip_duplicate(case, path)
     g = case.gpu
     c = case.cfg
     g.set_path(path)
@@ -144,9 +156,9 @@ def test_expert_stages(case, path):
     assert e_h <= TOL and e_o <= TOL and e_y <= TOL, (e_h, e_o, e_y)
 
 
-@pytest.mark.parametrize("path", [moe.MOE_PATH_AUTO, moe.MOE_PATH_SKINNY, moe.MOE_PATH_TILED],
-                         ids=["auto", "skinny", "tiled"])
+@pytest.mark.parametrize("path", [moe.MOE_PATH_AUTO] + STAGE_PATHS, ids=["auto", "skinny", "tiled", "tiled_mx"])
 def test_forward(case, path):
+    _skip_duplicate(case, path)
     g = case.gpu
     g.set_path(path)
     g.y.fill_(0)
