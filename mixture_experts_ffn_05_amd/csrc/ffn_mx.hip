@@ -134,16 +134,24 @@ constexpr int MX_NBUF = 4;                   // LDS stages
 constexpr int MX_DIST = 3;                   // token loads run this many stages ahead
 constexpr int MX_WB = 4;                     // weight blocks per wave (128 rows)
 constexpr int MX_TB = 4;                     // token blocks per wave (128 tokens)
-constexpr int MX_XSLABS = 2 * MX_CODE_BYTES / 16;  // token code slabs per stage: 2 blocks x 3 chunks
-constexpr int MX_XL = MX_XSLABS * GM_BT * 16 / 1024 / MX_WAVES;  // token code loads per wave per stage (6)
+constexpr int MX_BAND = 4;                   // M-tiles per band of the tile order
+constexpr int MX_XCH = 2 * MX_CODE_BYTES / 16;  // 16-byte token code chunks per row and stage (6)
+constexpr int MX_XL = MX_XCH * GM_BT * 16 / 1024 / MX_WAVES;  // token code loads per wave per stage (6)
 constexpr int MX_SL = GM_BT * 4 / 256 / MX_WAVES;                // token scale loads per wave per stage (1)
 
 struct MxShared {
     uint8_t w[MX_NBUF][2][GM_BW][16];          // E2M1 codes: [block][row], 32 values per 16 B
     uint8_t ws[MX_NBUF][2][GM_BW];             // weight E8M0 scales [block][row]
-    uint8_t x[MX_NBUF][MX_XSLABS][GM_BT][16];  // token codes: slab 3b + c = chunk c of block b
+    uint8_t x[MX_NBUF][GM_BT][MX_XCH][16];     // token codes [row][chunk slot], see mx_chunk_slot
     uint8_t xs[MX_NBUF][GM_BT][2][2];          // token scales [row][block][hi, lo]
 };
+
+// Token code chunk j (0..5: chunks 0-2 of block 0, then of block 1) of tile
+// row r sits in slot (j - ((r / 8) % 2)) mod 6 of the row's 96 LDS bytes: the
+// 16 lanes of one LDS read pass (16 consecutive rows, one chunk) then cover
+// 16 distinct 4-bank groups, and the rows stay whole in LDS so that each
+// wave-wide global load reads whole row segments.
+__device__ __forceinline__ int mx_chunk_slot(int r, int j) { return (j + 6 - ((r >> 3) & 1)) % 6; }
 
 // One 32x32x64 block-scaled MFMA: E2M1 weights (format 4) by one E2M3 term
 // (format 2) of the tokens; the weight scale is byte 0 of wsc, the token
@@ -175,7 +183,7 @@ __global__ __launch_bounds__(MX_THREADS, 1) void mx_gemm_kernel(FfnArgs a)
     if (tile >= total) return;
     int local, mtiles, mt, ntile;
     const int e = gm_locate(a.offsets, a.E, nt, tile, &local, &mtiles);
-    gm_band(local, mtiles, nt, &mt, &ntile);
+    gm_band<MX_BAND>(local, mtiles, nt, &mt, &ntile);
     const int seg1 = a.offsets[e + 1], sbase = a.offsets[e] + mt * GM_BT;
     const int n0 = ntile * WCOLS;
 
@@ -193,17 +201,21 @@ __global__ __launch_bounds__(MX_THREADS, 1) void mx_gemm_kernel(FfnArgs a)
         else
             return (uint32_t)(s < seg1 ? s : 0);
     };
-    // ---- token codes and scales, straight into LDS.  Codes: wave w, load i
-    // fills slab q / 4 for tile rows 64 (q % 4) .. +63, q = w + 4 i; lane l
-    // takes row 64 (q % 4) + l.  Scales: wave w fills rows 64 w .. +63, lane
-    // l the 4 bytes (hi, lo of both blocks of the stage) of row 64 w + l.
-    // Byte offsets stay below 2^31 (the split arrays of one call are checked
-    // against that on the host).
+    // ---- token codes and scales, straight into LDS.  Codes: the tile's 256
+    // rows x 6 chunk slots are filled in order, 1 KB (64 slots) per wave-wide
+    // load; load i of wave w covers slots 64 (w + 4 i) .. +63, and the lane of
+    // slot s fetches the chunk that belongs there: row s / 6, chunk j with
+    // mx_chunk_slot(row, j) = s % 6.  Consecutive lanes so read consecutive
+    // 16-byte pieces of the same gathered row.  Scales: wave w fills rows
+    // 64 w .. +63, lane l the 4 bytes (hi, lo of both blocks of the stage) of
+    // row 64 w + l.  Byte offsets stay below 2^31 (the split arrays of one
+    // call are checked against that on the host).
     uint32_t xoff[MX_XL], soff[MX_SL];
 #pragma unroll
     for (int i = 0; i < MX_XL; ++i) {
-        const int q = wave + MX_WAVES * i, slab = q >> 2, row = 64 * (q & 3) + lane;
-        xoff[i] = act_row(row) * (uint32_t)(nkb * MX_CODE_BYTES) + (slab / 3) * MX_CODE_BYTES + (slab % 3) * 16;
+        const int slot = 64 * (wave + MX_WAVES * i) + lane, row = slot / MX_XCH, pos = slot % MX_XCH;
+        const int j = (pos + ((row >> 3) & 1)) % MX_XCH;  // inverse of mx_chunk_slot
+        xoff[i] = act_row(row) * (uint32_t)(nkb * MX_CODE_BYTES) + j * 16;
     }
 #pragma unroll
     for (int j = 0; j < MX_SL; ++j) soff[j] = act_row(64 * (wave + MX_WAVES * j) + lane) * (uint32_t)(nkb * 2);
@@ -215,11 +227,9 @@ __global__ __launch_bounds__(MX_THREADS, 1) void mx_gemm_kernel(FfnArgs a)
         const uint8_t* cb = a.a_codes + (size_t)kk * 2 * MX_CODE_BYTES;
         const uint8_t* sb = a.a_scales + (size_t)kk * 4;
 #pragma unroll
-        for (int i = 0; i < MX_XL; ++i) {
-            const int q = wave + MX_WAVES * i;
-            __builtin_amdgcn_global_load_lds((gptr_t)(cb + xoff[i]), (lptr_t)&sh.x[buf][q >> 2][64 * (q & 3)][0], 16,
-                                             0, 0);
-        }
+        for (int i = 0; i < MX_XL; ++i)
+            __builtin_amdgcn_global_load_lds((gptr_t)(cb + xoff[i]),
+                                             (lptr_t)(&sh.x[buf][0][0][0] + 1024 * (wave + MX_WAVES * i)), 16, 0, 0);
 #pragma unroll
         for (int j = 0; j < MX_SL; ++j)
             __builtin_amdgcn_global_load_lds((gptr_t)(sb + soff[j]), (lptr_t)&sh.xs[buf][64 * (wave + MX_WAVES * j)][0][0],
@@ -301,7 +311,8 @@ __global__ __launch_bounds__(MX_THREADS, 1) void mx_gemm_kernel(FfnArgs a)
     uint32_t fws[MX_WB], fxs[MX_TB];
     u32x8 fhi[MX_TB], flo[MX_TB];
     auto chunk = [&](int buf, int c, int t) {
-        return *reinterpret_cast<const u32x4*>(&sh.x[buf][3 * kg + c][128 * wt + 32 * t + r32][0]);
+        const int row = 128 * wt + 32 * t + r32;
+        return *reinterpret_cast<const u32x4*>(&sh.x[buf][row][mx_chunk_slot(row, 3 * kg + c)][0]);
     };
     auto cat = [](u32x4 a, u32x4 b) { return u32x8{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w}; };
     auto load_w = [&](int buf, int m) {

@@ -63,19 +63,20 @@ __device__ __forceinline__ int gm_total_tiles(const int32_t* __restrict__ offset
     return n * nt;
 }
 
-// Local tile -> (m-tile, n-tile): bands of GM_BAND m-tiles; inside a band the
+// Local tile -> (m-tile, n-tile): bands of BAND m-tiles; inside a band the
 // m-tiles of one n-tile are adjacent, then the next n-tile.
+template <int BAND = GM_BAND>
 __device__ __forceinline__ void gm_band(int local, int mtiles, int nt, int* m, int* n)
 {
-    const int full = mtiles / GM_BAND;
-    if (local < full * GM_BAND * nt) {
-        const int band = local / (GM_BAND * nt), rem = local % (GM_BAND * nt);
-        *n = rem / GM_BAND;
-        *m = band * GM_BAND + rem % GM_BAND;
+    const int full = mtiles / BAND;
+    if (local < full * BAND * nt) {
+        const int band = local / (BAND * nt), rem = local % (BAND * nt);
+        *n = rem / BAND;
+        *m = band * BAND + rem % BAND;
     } else {
-        const int rem = local - full * GM_BAND * nt, bm = mtiles - full * GM_BAND;
+        const int rem = local - full * BAND * nt, bm = mtiles - full * BAND;
         *n = rem / bm;
-        *m = full * GM_BAND + rem % bm;
+        *m = full * BAND + rem % bm;
     }
 }
 
