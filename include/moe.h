@@ -130,11 +130,14 @@ enum { MOE_WFMT_BF16 = 0, MOE_WFMT_MXFP4 = 1, MOE_WFMT_MXFP4_PACKED = 2 };
  *                  from the bf16 path's (hi + lo keeps about as much of each
  *                  activation as bf16 does; both stay within the layer's
  *                  1e-2 * max|y| tolerance), so the two give different bits.
- * TILED (and AUTO in the tiled regime) takes TILED_DEQUANT, the faster of the
- * two on the 20b prefill shapes; TILED_MX runs only when asked for.  For bf16
- * weights all tiled paths are the bf16 kernel except TILED_MX, which returns
- * MOE_ERR_UNSUPPORTED.  Every path computes the same function; forcing one is
- * for testing and tuning. */
+ * TILED (and AUTO in the tiled regime) takes TILED_MX wherever it applies,
+ * else TILED_DEQUANT: on the 20b MXFP4 prefill the MX kernel is the faster of
+ * the two.  moe_gate_up and moe_down then need the workspace (the split
+ * activations live there); moe_grouped_ffn and moe_forward keep h only in its
+ * split form, made by the gate/up kernel, with the same bits as the stage
+ * entry points give.  For bf16 weights all tiled paths are the bf16 kernel
+ * except TILED_MX, which returns MOE_ERR_UNSUPPORTED.  Every path computes
+ * the same function; forcing one is for testing and tuning. */
 enum {
     MOE_PATH_AUTO = 0,
     MOE_PATH_SKINNY = 1,

@@ -18,18 +18,21 @@
 // stored, with no decode.
 //
 // mx_split_kernel makes the two terms once per activation row (x before the
-// gate/up GEMM, h before the down GEMM); mx_gemm_kernel is the grouped GEMM,
-// with the tile schedule, tile shape, gate/up pairing and epilogues of the
-// bf16 tiled kernel (ffn_tiled.hip):
-//   tile 256 weight rows x 256 tokens, 8 waves in 2 (weight halves) x 4
-//   (token quarters), each wave 4 x 2 blocks of 32 x 32 in 128 accumulators;
-//   K advances in stages of 64 (two MX blocks, one MFMA per block pair and
-//   term) through a ring of 4 LDS buffers.
-// Token codes and scales are loaded straight into LDS (global_load_lds) three
-// stages ahead; weight codes and scales take registers two stages ahead (so
-// that row-major and packed MXFP4 orders can be addressed alike).  LDS holds
-// each operand as slabs of 16 bytes per row, [slab][row][16 B], so the 16
-// lanes of one LDS read pass cover 256 consecutive bytes (no bank conflicts).
+// gate/up GEMM, and h before the down GEMM where h arrives as bf16; the layer
+// entry points have the gate/up epilogue split h itself).  mx_gemm_kernel is
+// the grouped GEMM, with the tile schedule and gate/up pairing of the bf16
+// tiled kernel (tile_sched.h):
+//   tile 256 weight rows x 256 tokens, 4 waves (one per SIMD) as 2 weight
+//   halves x 2 token halves, each wave 4 x 4 blocks of 32 x 32 in 256
+//   accumulators; K advances in stages of 64 (two MX blocks: one MFMA per
+//   block pair and term) through a ring of 4 LDS buffers.
+// Token codes and scales go straight into LDS (global_load_lds) three stages
+// ahead.  Each tile row stays whole in LDS (its six 16-byte chunks of a stage
+// in rotated slots, see mx_chunk_slot), so one wave-wide load reads
+// consecutive 16-byte pieces of gathered rows and the fragment reads are free
+// of bank conflicts.  Weight codes and scales take registers two stages ahead
+// (so that the row-major and packed MXFP4 orders are addressed alike) and are
+// stored to LDS as [block][row][16 B].
 #include <string.h>
 
 #include <type_traits>
@@ -60,27 +63,15 @@ __device__ __forceinline__ int mx_shared_exponent(uint32_t amax_exp_field)
     return min(max((int)amax_exp_field - 2, 1), 254);
 }
 
-// One lane per 32-element block.  hi's codes come from the hardware
-// conversion (round to nearest even of x / 2^(S-127) onto E2M3, saturating
-// at 7.5); hi's values are formed the same way in fp32 to get lo = x - hi,
-// which is exact and exactly a bf16 value (x and hi are both multiples of
-// x's last bit, and |lo| <= |x|).
-__global__ __launch_bounds__(MXS_THREADS) void mx_split_kernel(const uint16_t* __restrict__ in, int64_t nblocks,
-                                                                uint8_t* __restrict__ codes,
-                                                                uint8_t* __restrict__ scales)
+// Both terms of one 32-element block, w = its bf16 values in order, two per
+// dword (element 2i in the low half of w[i]).  hi's codes come from the
+// hardware conversion (round to nearest even of x / 2^(S-127) onto E2M3,
+// saturating at 7.5); hi's values are formed the same way in fp32 to get
+// lo = x - hi, which is exact and exactly a bf16 value (x and hi are both
+// multiples of x's last bit, and |lo| <= |x|).  Writes the 48 code bytes as
+// three 16-byte pieces and returns the two scale bytes (hi in the low byte).
+__device__ __forceinline__ uint32_t mx_split_block(const uint32_t (&w)[16], u32x4 (&out)[3])
 {
-    const int64_t blk = (int64_t)blockIdx.x * MXS_THREADS + threadIdx.x;
-    if (blk >= nblocks) return;
-    const u32x4* src = reinterpret_cast<const u32x4*>(in + blk * 32);
-    uint32_t w[16];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const u32x4 v = __builtin_nontemporal_load(src + i);
-        w[4 * i] = v.x;
-        w[4 * i + 1] = v.y;
-        w[4 * i + 2] = v.z;
-        w[4 * i + 3] = v.w;
-    }
     uint32_t amax = 0;  // largest |x| as bf16 bits
 #pragma unroll
     for (int i = 0; i < 16; ++i) amax = max(amax, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
@@ -110,11 +101,36 @@ __global__ __launch_bounds__(MXS_THREADS) void mx_split_kernel(const uint16_t* _
         lw[i] = (__float_as_uint(lo[2 * i]) >> 16) | (__float_as_uint(lo[2 * i + 1]) & 0xFFFF0000u);
     const u32x6 ch = __builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(__builtin_bit_cast(bf16x32, w), sc);
     const u32x6 cl = __builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(__builtin_bit_cast(bf16x32, lw), sc2);
+    out[0] = u32x4{ch[0], ch[1], ch[2], ch[3]};
+    out[1] = u32x4{ch[4], ch[5], cl[0], cl[1]};
+    out[2] = u32x4{cl[2], cl[3], cl[4], cl[5]};
+    return (uint32_t)S | ((uint32_t)S2 << 8);
+}
+
+// One lane per 32-element block.
+__global__ __launch_bounds__(MXS_THREADS) void mx_split_kernel(const uint16_t* __restrict__ in, int64_t nblocks,
+                                                                uint8_t* __restrict__ codes,
+                                                                uint8_t* __restrict__ scales)
+{
+    const int64_t blk = (int64_t)blockIdx.x * MXS_THREADS + threadIdx.x;
+    if (blk >= nblocks) return;
+    const u32x4* src = reinterpret_cast<const u32x4*>(in + blk * 32);
+    uint32_t w[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const u32x4 v = __builtin_nontemporal_load(src + i);
+        w[4 * i] = v.x;
+        w[4 * i + 1] = v.y;
+        w[4 * i + 2] = v.z;
+        w[4 * i + 3] = v.w;
+    }
+    u32x4 c[3];
+    const uint32_t sb = mx_split_block(w, c);
     u32x4* dst = reinterpret_cast<u32x4*>(codes + blk * MX_CODE_BYTES);
-    dst[0] = u32x4{ch[0], ch[1], ch[2], ch[3]};
-    dst[1] = u32x4{ch[4], ch[5], cl[0], cl[1]};
-    dst[2] = u32x4{cl[2], cl[3], cl[4], cl[5]};
-    *reinterpret_cast<uint16_t*>(scales + blk * 2) = (uint16_t)(S | (S2 << 8));
+    dst[0] = c[0];
+    dst[1] = c[1];
+    dst[2] = c[2];
+    *reinterpret_cast<uint16_t*>(scales + blk * 2) = (uint16_t)sb;
 }
 
 hipError_t launch_mx_split(const uint16_t* in, int64_t rows, int K, uint8_t* codes, uint8_t* scales, hipStream_t s)
@@ -164,7 +180,7 @@ __device__ __forceinline__ f32x16 mfma_mx(u32x4 w, u32x6 x, uint32_t wsc, uint32
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 2, 0, (int)wsc, TERM, (int)xsc);
 }
 
-template <bool PACKED, bool GATE_UP>
+template <bool PACKED, bool GATE_UP, bool SPLIT_OUT>
 __global__ __launch_bounds__(MX_THREADS, 1) void mx_gemm_kernel(FfnArgs a)
 {
     __shared__ __attribute__((aligned(16))) MxShared sh;
@@ -402,6 +418,55 @@ __global__ __launch_bounds__(MX_THREADS, 1) void mx_gemm_kernel(FfnArgs a)
     // ---- epilogue: for each (m, t) the lane holds tile weight rows
     // 128ww + 32m + 8(r/4) + 4(lane/32) + r%4 (r = 0..15) of token
     // 128wt + 32t + lane%32.
+    if constexpr (GATE_UP && SPLIT_OUT) {
+        // h goes out as the down GEMM's split activations (the bf16 h values
+        // split as mx_split_kernel would split them).  Output columns
+        // n0 + 64ww + 32m .. +31 (m = 0, 1) are one 32-value block of an h row,
+        // held half by lane l (columns 8q + 0..3) and half by lane l ^ 32
+        // (8q + 4..7).  The lane pair trades halves so that lane l splits
+        // block 0 and lane l ^ 32 block 1 of its token row.
+        const int nkb_out = NOUT / 32;
+        const int kb = (n0 + 64 * ww) / 32 + kg;
+        const bool cols_in = n0 + 64 * ww < NOUT;  // NOUT % 64 == 0: both blocks in or out
+#pragma unroll
+        for (int t = 0; t < MX_TB; ++t) {
+            uint32_t hv[2][8];  // [block m][dword 2q + j]: bf16 pairs of columns 8q + 4kg + 2j, +1
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                const f32x16& g = acc[m][t];
+                const f32x16& u = acc[m + 2][t];
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    hv[m][i] = pack_bf16x2(silu(g[2 * i]) * u[2 * i], silu(g[2 * i + 1]) * u[2 * i + 1]);
+            }
+            uint32_t mine[8], theirs[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                mine[i] = kg ? hv[1][i] : hv[0][i];
+                theirs[i] = (uint32_t)__builtin_amdgcn_ds_bpermute((lane ^ 32) * 4, (int)(kg ? hv[0][i] : hv[1][i]));
+            }
+            uint32_t wv[16];  // the block's 32 values in column order
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                wv[4 * q + 0] = kg ? theirs[2 * q] : mine[2 * q];
+                wv[4 * q + 1] = kg ? theirs[2 * q + 1] : mine[2 * q + 1];
+                wv[4 * q + 2] = kg ? mine[2 * q] : theirs[2 * q];
+                wv[4 * q + 3] = kg ? mine[2 * q + 1] : theirs[2 * q + 1];
+            }
+            u32x4 c[3];
+            const uint32_t sb = mx_split_block(wv, c);
+            const int s = sbase + 128 * wt + 32 * t + r32;
+            if (s < seg1 && cols_in) {
+                const size_t blk = (size_t)s * nkb_out + kb;
+                u32x4* dst = reinterpret_cast<u32x4*>(a.out_codes + blk * MX_CODE_BYTES);
+                dst[0] = c[0];
+                dst[1] = c[1];
+                dst[2] = c[2];
+                *reinterpret_cast<uint16_t*>(a.out_scales + blk * 2) = (uint16_t)sb;
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int t = 0; t < MX_TB; ++t) {
         const int s = sbase + 128 * wt + 32 * t + r32;
@@ -444,7 +509,7 @@ __global__ __launch_bounds__(MX_THREADS, 1) void mx_gemm_kernel(FfnArgs a)
 
 bool mx_supported(int H, int I) { return H % 64 == 0 && I % 64 == 0; }
 
-template <bool PACKED, bool GATE_UP>
+template <bool PACKED, bool GATE_UP, bool SPLIT_OUT>
 static hipError_t launch_mx(const FfnArgs& a, hipStream_t s)
 {
     const int NOUT = GATE_UP ? a.I : a.H;
@@ -453,18 +518,20 @@ static hipError_t launch_mx(const FfnArgs& a, hipStream_t s)
     const long long mt_bound = ((long long)a.T * a.k + GM_BT - 1) / GM_BT + a.E;
     long long grid = nt * mt_bound;
     grid = (grid + 7) / 8 * 8;
-    hipLaunchKernelGGL((mx_gemm_kernel<PACKED, GATE_UP>), dim3((unsigned)grid), dim3(MX_THREADS), 0, s, a);
+    hipLaunchKernelGGL((mx_gemm_kernel<PACKED, GATE_UP, SPLIT_OUT>), dim3((unsigned)grid), dim3(MX_THREADS), 0, s, a);
     return hipGetLastError();
 }
 
 hipError_t launch_gate_up_mx(const FfnArgs& a, hipStream_t s)
 {
-    return a.wfmt == 2 ? launch_mx<true, true>(a, s) : launch_mx<false, true>(a, s);
+    if (a.out_codes)
+        return a.wfmt == 2 ? launch_mx<true, true, true>(a, s) : launch_mx<false, true, true>(a, s);
+    return a.wfmt == 2 ? launch_mx<true, true, false>(a, s) : launch_mx<false, true, false>(a, s);
 }
 
 hipError_t launch_down_mx(const FfnArgs& a, hipStream_t s)
 {
-    return a.wfmt == 2 ? launch_mx<true, false>(a, s) : launch_mx<false, false>(a, s);
+    return a.wfmt == 2 ? launch_mx<true, false, false>(a, s) : launch_mx<false, false, false>(a, s);
 }
 
 }  // namespace moe

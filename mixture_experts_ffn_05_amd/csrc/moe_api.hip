@@ -150,9 +150,14 @@ bool use_skinny(const moe_dims& d)
 }
 
 // Tiled regime on the MX matrix cores (MXFP4 weights; see MOE_PATH_TILED_MX):
-// only when asked for, since on the 20b prefill shapes the bf16-decode kernel
-// is still the faster one.
-bool use_mx(const moe_dims& d) { return d.path == MOE_PATH_TILED_MX && mx_fits(d); }
+// when asked for, and for TILED and AUTO in the tiled regime wherever it
+// applies (on the 20b MXFP4 prefill it takes 0.82x the time of the
+// bf16-decode kernel in the packed order, 0.97x row-major).
+bool use_mx(const moe_dims& d)
+{
+    if (!mx_fits(d)) return false;
+    return d.path == MOE_PATH_TILED_MX || d.path == MOE_PATH_TILED || (d.path == MOE_PATH_AUTO && !use_skinny(d));
+}
 
 moe::FfnArgs ffn_args(const moe_dims& d)
 {
@@ -204,9 +209,11 @@ int do_permute(const moe_dims& d, const int32_t* idx, int32_t* off, int32_t* sp,
 }
 
 // The MX path splits the activations into the workspace first (x: T rows,
-// h: P rows), then runs the MX grouped GEMM on them.
+// h: P rows), then runs the MX grouped GEMM on them.  With h_split the MX
+// gate/up kernel writes h already split (into the workspace regions that
+// do_down reads with h_split) and no bf16 h at all; results are the same bits.
 int do_gate_up(const moe_dims& d, const void* x, const int32_t* off, const int32_t* sp, const moe_expert_weights& w,
-               void* h, void* ws, hipStream_t s)
+               void* h, void* ws, hipStream_t s, bool h_split = false)
 {
     moe::FfnArgs a = ffn_args(d);
     a.x = static_cast<const uint16_t*>(x);
@@ -219,6 +226,10 @@ int do_gate_up(const moe_dims& d, const void* x, const int32_t* off, const int32
         const Layout L = layout_for(d);
         a.a_codes = region<uint8_t>(ws, L.xs_codes);
         a.a_scales = region<uint8_t>(ws, L.xs_scales);
+        if (h_split) {
+            a.out_codes = region<uint8_t>(ws, L.hs_codes);
+            a.out_scales = region<uint8_t>(ws, L.hs_scales);
+        }
         int rc = hip_status(moe::launch_mx_split(a.x, d.T, d.H, region<uint8_t>(ws, L.xs_codes),
                                                  region<uint8_t>(ws, L.xs_scales), s));
         if (rc) return rc;
@@ -228,7 +239,7 @@ int do_gate_up(const moe_dims& d, const void* x, const int32_t* off, const int32
 }
 
 int do_down(const moe_dims& d, const void* h, const int32_t* off, const moe_expert_weights& w, void* ys, void* ws,
-            hipStream_t s)
+            hipStream_t s, bool h_split = false)
 {
     moe::FfnArgs a = ffn_args(d);
     a.offsets = off;
@@ -240,9 +251,12 @@ int do_down(const moe_dims& d, const void* h, const int32_t* off, const moe_expe
         const Layout L = layout_for(d);
         a.a_codes = region<uint8_t>(ws, L.hs_codes);
         a.a_scales = region<uint8_t>(ws, L.hs_scales);
-        int rc = hip_status(moe::launch_mx_split(a.a_rows, (int64_t)d.T * d.k, d.I, region<uint8_t>(ws, L.hs_codes),
-                                                 region<uint8_t>(ws, L.hs_scales), s));
-        if (rc) return rc;
+        if (!h_split) {
+            int rc = hip_status(moe::launch_mx_split(a.a_rows, (int64_t)d.T * d.k, d.I,
+                                                     region<uint8_t>(ws, L.hs_codes),
+                                                     region<uint8_t>(ws, L.hs_scales), s));
+            if (rc) return rc;
+        }
         return hip_status(moe::launch_down_mx(a, s));
     }
     return hip_status(use_skinny(d) ? moe::launch_down_skinny(a, s) : moe::launch_down_tiled(a, s));
@@ -481,8 +495,8 @@ int moe_grouped_ffn(const moe_dims* dims, const void* x, const int32_t* expert_o
         return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
     void* h = region<void>(workspace, layout_for(d).h);
-    if ((rc = do_gate_up(d, x, expert_offsets, sorted_pairs, *weights, h, workspace, s))) return rc;
-    return do_down(d, h, expert_offsets, *weights, y_sorted, workspace, s);
+    if ((rc = do_gate_up(d, x, expert_offsets, sorted_pairs, *weights, h, workspace, s, true))) return rc;
+    return do_down(d, h, expert_offsets, *weights, y_sorted, workspace, s, true);
 }
 
 int moe_combine(const moe_dims* dims, const void* y_sorted, const int32_t* pair_rank, const float* topk_w, void* y,
@@ -521,8 +535,8 @@ int moe_forward(const moe_dims* dims, const void* x, const void* w_router, const
     void* h = region<void>(workspace, L.h);
     void* ys = region<void>(workspace, L.y_sorted);
     if ((rc = do_route_permute(d, x, w_router, idx, w, off, sp, pr, workspace, s))) return rc;
-    if ((rc = do_gate_up(d, x, off, sp, *weights, h, workspace, s))) return rc;
-    if ((rc = do_down(d, h, off, *weights, ys, workspace, s))) return rc;
+    if ((rc = do_gate_up(d, x, off, sp, *weights, h, workspace, s, true))) return rc;
+    if ((rc = do_down(d, h, off, *weights, ys, workspace, s, true))) return rc;
     return hip_status(moe::launch_combine(d.T, d.H, d.k, static_cast<const uint16_t*>(ys), pr, w,
                                           static_cast<uint16_t*>(y), s));
 }

@@ -55,6 +55,10 @@ struct FfnArgs {
     const uint8_t* a_codes;
     const uint8_t* a_scales;
     uint16_t* out;              // gate/up: h [P][I]; down: y_sorted [P][H]
+    // MX gate/up only, optional: h written split for the down GEMM instead of
+    // as bf16 (codes [P][I/32][48], scales [P][I/32][2]); out is then unused
+    uint8_t* out_codes;
+    uint8_t* out_scales;
     uint16_t* gu_out;           // tiled gate/up only, optional: g then u [P][2I] (bf16), for the backward
     // weight-gradient mode of the tiled kernel: C[e][m][n] = sum_j A_e[m][j] B_e[n][j]
     // (fp32), A_e = wg_a + wg_M * padoff[e] ([wg_M][Kpad_e]), B_e likewise with wg_N

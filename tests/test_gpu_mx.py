@@ -11,7 +11,9 @@ cores with the activations split into two MXFP6 (E2M3) terms.
   for the 20b MXFP4 prefill (32768 tokens, 512 checked) and decode configs in
   the row-major and the packed order, and ragged shapes (segments over several
   256-token tiles and tails, output widths off the 256-row tile, a single
-  64-wide K stage, E = 1, k = E)."""
+  64-wide K stage, E = 1, k = E).
+- moe_forward and moe_grouped_ffn (h split inside the gate/up kernel) against
+  the stage entry points (bf16 h, split by moe_down): identical bits."""
 from __future__ import annotations
 
 import numpy as np
@@ -143,6 +145,7 @@ def test_mx_ragged(shape, packed):
     assert np.array_equal(g.topk_idx.cpu().numpy(), idx_ref)
     e = rel_err(bf16_dev_to_f64(g.y), y_ref)
     assert e <= TOL, e
+    y_fused = g.y.clone()
     # stage by stage on the same path: h and y_sorted per pair
     g.stages()
     torch.cuda.synchronize()
@@ -151,6 +154,14 @@ def test_mx_ragged(shape, packed):
     e_o = rel_err(bf16_dev_to_f64(g.y_sorted)[pr], o_ref.reshape(-1, c.H))
     print(f"[mx] {c.name} rel err y {e:.2e} h {e_h:.2e} y_sorted {e_o:.2e}")
     assert e_h <= TOL and e_o <= TOL, (e_h, e_o)
+    # moe_forward and moe_grouped_ffn split h inside the gate/up kernel; the
+    # stage entry points write bf16 h and split it in the down stage: same bits
+    assert torch.equal(y_fused, g.y)
+    ys_stages = g.y_sorted.clone()
+    g.y_sorted.fill_(0)
+    g.grouped_ffn()
+    torch.cuda.synchronize()
+    assert torch.equal(ys_stages, g.y_sorted)
 
 
 @pytest.mark.parametrize("name", ["20b_mxfp4_prefill", "20b_mxfp4_prefill+packed", "20b_mxfp4_decode+packed"])
@@ -174,6 +185,9 @@ def test_mx_configs(name):
     g.forward()
     torch.cuda.synchronize()
     assert torch.equal(y1, g.y)  # deterministic
+    g.stages()  # h written as bf16 and split by the down stage: the same bits as the fused split
+    torch.cuda.synchronize()
+    assert torch.equal(y1, g.y)
 
 
 def test_mx_refuses_what_it_cannot_run():

@@ -123,17 +123,21 @@ def test_permute(case):
     assert np.array_equal(g.pair_rank.cpu().numpy(), case.pr)
 
 
-# For MXFP4 weights TILED_MX runs the MX-core kernel and TILED the bf16-decode
-# one; for bf16 weights TILED is the only tiled kernel.
-STAGE_PATHS = [moe.MOE_PATH_SKINNY, moe.MOE_PATH_TILED, moe.MOE_PATH_TILED_MX]
+# For MXFP4 weights TILED_MX runs the MX-core kernel (so does TILED, where the
+# MX kernel applies) and TILED_DEQUANT the bf16-decode one; for bf16 weights
+# TILED is the only tiled kernel.
+STAGE_PATHS = [moe.MOE_PATH_SKINNY, moe.MOE_PATH_TILED, moe.MOE_PATH_TILED_DEQUANT, moe.MOE_PATH_TILED_MX]
+STAGE_IDS = ["skinny", "tiled", "tiled_dequant", "tiled_mx"]
 
 
 def _skip_duplicate(case, path):
-    if path == moe.MOE_PATH_TILED_MX and case.cfg.wfmt == 0:
-        pytest.skip("bf16 weights have no MX-core path")
+    if case.cfg.wfmt == 0 and path in (moe.MOE_PATH_TILED_DEQUANT, moe.MOE_PATH_TILED_MX):
+        pytest.skip("bf16 weights: one tiled kernel (TILED)")
+    if case.cfg.wfmt != 0 and path == moe.MOE_PATH_TILED:
+        pytest.skip("MXFP4 weights: TILED runs the TILED_MX kernel")
 
 
-@pytest.mark.parametrize("path", STAGE_PATHS, ids=["skinny", "tiled", "tiled_mx"])
+@pytest.mark.parametrize("path", STAGE_PATHS, ids=STAGE_IDS)
 def test_expert_stages(case, path):
     """gate/up+SwiGLU -> h, down -> y_sorted, combine -> y, each against the oracle."""
     _skip_duplicate(case, path)
@@ -156,7 +160,7 @@ def test_expert_stages(case, path):
     assert e_h <= TOL and e_o <= TOL and e_y <= TOL, (e_h, e_o, e_y)
 
 
-@pytest.mark.parametrize("path", [moe.MOE_PATH_AUTO] + STAGE_PATHS, ids=["auto", "skinny", "tiled", "tiled_mx"])
+@pytest.mark.parametrize("path", [moe.MOE_PATH_AUTO] + STAGE_PATHS, ids=["auto"] + STAGE_IDS)
 def test_forward(case, path):
     _skip_duplicate(case, path)
     g = case.gpu
