@@ -680,8 +680,15 @@ __device__ __forceinline__ void s4_step(const FfnArgs& a, const S4Experts& x, in
     c1 = c2;
 }
 
-// Persistent over items: wave w takes items w, w + nw, ... (item = touched
-// expert x 32-row tile; gate/up N = I, K = H; down N = H, K = I).
+// Persistent over items (item = touched expert x 32-row tile; gate/up N = I,
+// K = H; down N = H, K = I); wave w takes items w, w + nw, ...  gate/up: all
+// resident waves, numbered block by block (the 4 waves of a block stream
+// neighbouring rows).  down: the items are dealt out in equal rounds -- with
+// R rounds of the resident waves needed, only ceil(items / R) waves take part
+// and the rest exit, so that no short last round runs on a fraction of the
+// waves; these are numbered across blocks first, to spread them over all
+// CUs.  (Measured on the 20b decode shapes: each choice is the faster one for
+// its projection.)
 template <int TG, bool GATE_UP>
 __global__ __launch_bounds__(S4_THREADS, 2) void skinny4_kernel(FfnArgs a)
 {
@@ -689,8 +696,15 @@ __global__ __launch_bounds__(S4_THREADS, 2) void skinny4_kernel(FfnArgs a)
     const int tiles = GATE_UP ? a.I / 16 : a.H / 32;
     const S4Experts x = s4_experts(a);
     const int n_items = x.active * tiles;
-    const int nw = gridDim.x * S4_WPB;
-    const int w = blockIdx.x * S4_WPB + __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);  // uniform per wave
+    const int nw_all = gridDim.x * S4_WPB;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);  // uniform per wave
+    int nw = nw_all, w = blockIdx.x * S4_WPB + wave;
+    if constexpr (!GATE_UP) {
+        const int rounds = (n_items + nw_all - 1) / nw_all;
+        nw = rounds > 0 ? (n_items + rounds - 1) / rounds : 1;
+        w = wave * gridDim.x + blockIdx.x;
+        if (w >= nw) return;
+    }
     S4Cursor c0 = s4_item(x, w, n_items, tiles);
     if (c0.item < 0) return;  // uniform per wave
 

@@ -188,53 +188,48 @@ __device__ __forceinline__ bool ranks_before(double v, int i, double bv, int bi)
     return v > bv || (v == bv && i < bi);
 }
 
-// Per-wave LDS for wave_topk_softmax_rank.
-struct TopkScratch {
-    double v[WAVE];    // the token's logits, lane e holding expert e
-    double sel_v[8];   // selected logits by slot
-};
+// Lane l's value of v (l uniform), through two scalar lane reads.
+__device__ __forceinline__ double readlane_f64(double v, int l)
+{
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
 
 // Top-k for E <= 64 by one wave, lane e holding expert e: each lane counts
 // the experts that rank before its own (larger logit, or equal logit and a
-// lower index) over all E logits staged in LDS, so its rank is exact and the
-// k lanes with rank < k own the slots -- no serial arg-max rounds.  Then the
-// softmax over the k selected, summed in slot order exactly as
-// wave_topk_softmax does, so both give the same weights.  Lane j writes slot j.
-__device__ __forceinline__ void wave_topk_softmax_rank(const double* row, int E, int k, int32_t* __restrict__ idx_out,
-                                                       float* __restrict__ w_out, TopkScratch& sc)
+// lower index) over all E logits, read lane by lane from registers, so its
+// rank is exact and the k lanes with rank < k own the slots -- no serial
+// arg-max rounds.  Then the softmax over the k selected: each selected lane
+// takes its own exp, and the sum runs in slot order exactly as
+// wave_topk_softmax's does, so both give the same weights.  The lane of slot
+// j writes slot j; returns this lane's slot, or -1.
+__device__ __forceinline__ int wave_topk_softmax_rank(const double* row, int E, int k, int32_t* __restrict__ idx_out,
+                                                      float* __restrict__ w_out)
 {
     const int e = lane_id();
     const double v = e < E ? rank_key(row[e]) : -__builtin_inf();
-    sc.v[e] = v;
-    __builtin_amdgcn_wave_barrier();
     int rank = 0;
-    for (int j = 0; j < E; ++j) rank += ranks_before(sc.v[j], j, v, e) ? 1 : 0;
-    if (e < E && rank < k) {
-        sc.sel_v[rank] = v;
-        idx_out[rank] = e;
-    }
-    __builtin_amdgcn_wave_barrier();
-    double sv[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) sv[j] = j < k ? sc.sel_v[j] : 0.0;
+    for (int j = 0; j < E; ++j) rank += ranks_before(readlane_f64(v, j), j, v, e) ? 1 : 0;
+    const bool sel = e < E && rank < k;
+    const double v0 = readlane_f64(v, (int)__builtin_ctzll(ballot(sel && rank == 0)));
+    const double ex = sel ? exp(v - v0) : 0.0;
     double z = 0.0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-        if (j < k) z += exp(sv[j] - sv[0]);
-    if (e < k) {
-        double mine = sv[0];
-#pragma unroll
-        for (int j = 1; j < 8; ++j)
-            if (e == j) mine = sv[j];
-        w_out[e] = (float)(exp(mine - sv[0]) / z);
+    for (int j = 0; j < k; ++j) z += readlane_f64(ex, (int)__builtin_ctzll(ballot(sel && rank == j)));
+    if (sel) {
+        idx_out[rank] = e;
+        w_out[rank] = (float)(ex / z);
     }
+    return sel ? rank : -1;
 }
 
 // Top-k of one token's E logits (row: global or LDS) by one wave: k rounds of
 // a wave-wide arg-max (each lane owns experts lane, lane+64, ...), then the
-// softmax over the k selected.  Lane j writes slot j.
-__device__ __forceinline__ void wave_topk_softmax(const double* row, int E, int k, int32_t* __restrict__ idx_out,
-                                  float* __restrict__ w_out)
+// softmax over the k selected.  Lane j writes slot j and returns its expert
+// (other lanes -1).
+__device__ __forceinline__ int wave_topk_softmax(const double* row, int E, int k, int32_t* __restrict__ idx_out,
+                                                 float* __restrict__ w_out)
 {
     const int lane = lane_id();
     double v[4];
@@ -279,13 +274,16 @@ __device__ __forceinline__ void wave_topk_softmax(const double* row, int E, int 
 #pragma unroll
     for (int j = 0; j < 8; ++j)
         if (j < k) z += exp(sel_v[j] - sel_v[0]);
+    int mine = -1;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         if (j < k && lane == j) {
             idx_out[j] = sel_i[j];
             w_out[j] = (float)(exp(sel_v[j] - sel_v[0]) / z);
+            mine = sel_i[j];
         }
     }
+    return mine;
 }
 
 }  // namespace moe

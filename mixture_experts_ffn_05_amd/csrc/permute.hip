@@ -156,22 +156,26 @@ __global__ __launch_bounds__(PB_THREADS) void permute_small_kernel(int P, int E,
 }
 
 // Small batches: top-k selection of every token (one wave per token, logits
-// [T][E] from the router) followed by the permutation, in one workgroup.
+// [T][E] from the router) followed by the permutation, in one workgroup.  The
+// selected experts also go to LDS, where the permutation reads them.
 __global__ __launch_bounds__(PB_THREADS) void select_permute_small_kernel(
     int T, int E, int k, const double* __restrict__ logits, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_w, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs,
     int32_t* __restrict__ pair_rank)
 {
-    __shared__ TopkScratch sc[PB_WAVES];
+    __shared__ int32_t keys[SMALL_P];
     for (int t = threadIdx.x / WAVE; t < T; t += PB_WAVES) {
-        if (E <= WAVE)
-            wave_topk_softmax_rank(logits + (size_t)t * E, E, k, topk_idx + (size_t)t * k, topk_w + (size_t)t * k,
-                                   sc[threadIdx.x / WAVE]);
-        else
-            wave_topk_softmax(logits + (size_t)t * E, E, k, topk_idx + (size_t)t * k, topk_w + (size_t)t * k);
+        int32_t* idx = topk_idx + (size_t)t * k;
+        if (E <= WAVE) {
+            const int slot = wave_topk_softmax_rank(logits + (size_t)t * E, E, k, idx, topk_w + (size_t)t * k);
+            if (slot >= 0) keys[t * k + slot] = (int32_t)lane_id();
+        } else {
+            const int ex = wave_topk_softmax(logits + (size_t)t * E, E, k, idx, topk_w + (size_t)t * k);
+            if (ex >= 0) keys[t * k + lane_id()] = ex;
+        }
     }
-    __syncthreads();  // this workgroup's topk_idx stores are visible to it after the barrier
-    permute_block(T * k, E, topk_idx, offsets, sorted_pairs, pair_rank);
+    __syncthreads();
+    permute_block(T * k, E, keys, offsets, sorted_pairs, pair_rank);
 }
 
 // Pass 1 of the multi-block path: chunk b = blockIdx.x ranks its pairs and

@@ -238,12 +238,10 @@ __global__ __launch_bounds__(256) void router_select_kernel(int T, int E, int k,
                                                             int32_t* __restrict__ topk_idx,
                                                             float* __restrict__ topk_w)
 {
-    __shared__ TopkScratch sc[256 / WAVE];
     const int t = (int)((blockIdx.x * blockDim.x + threadIdx.x) / WAVE);
     if (t >= T) return;
     if (E <= WAVE)
-        wave_topk_softmax_rank(logits + (size_t)t * E, E, k, topk_idx + (size_t)t * k, topk_w + (size_t)t * k,
-                               sc[threadIdx.x / WAVE]);
+        wave_topk_softmax_rank(logits + (size_t)t * E, E, k, topk_idx + (size_t)t * k, topk_w + (size_t)t * k);
     else
         wave_topk_softmax(logits + (size_t)t * E, E, k, topk_idx + (size_t)t * k, topk_w + (size_t)t * k);
 }
