@@ -49,6 +49,10 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0   # dense bf16 MFMA
 FP4_PEAK_TFLOPS = 10100.0   # dense MXFP4 MFMA
+# The MX path multiplies every product twice (E2M1 weights by the hi and the lo
+# E2M3 term of the activations, both at the fp4/fp6 rate), so the layer's own
+# FLOPs can run at most at half the fp4 peak: the fp8 rate.
+MX_TWO_TERM_PEAK_TFLOPS = FP4_PEAK_TFLOPS / 2
 METRIC = "MoE-layer tokens/s + % HBM peak (decode, 16 tok) and % MFMA peak (prefill)"
 MALL_BYTES = 256 << 20
 PROFILE_DIR = os.path.join(ROOT, "profiles")
@@ -277,6 +281,25 @@ def layer_flops(cfg):
     """Algorithmic FLOPs: 2*P*3*H*I for the experts + 2*T*E*H for the router."""
     P = cfg.T * cfg.k
     return 2.0 * P * 3 * cfg.H * cfg.I + 2.0 * cfg.T * cfg.E * cfg.H, 2.0 * P * 2 * cfg.I * cfg.H
+
+
+def prefill_record(cfg, sec, stages, mx: bool):
+    """A prefill line: tokens/s, us, TFLOP/s of the layer's own FLOPs, and the
+    fractions of the peaks that bound it (bf16 MFMA; for the MX kernel also
+    the fp4 peak and its two-term ceiling, half of it)."""
+    fl, fl_gu = layer_flops(cfg)
+    tf = fl / sec / 1e12
+    rec = {"kernel": ("MX matrix cores, E2M1 weights x two E2M3 activation terms" if mx
+                      else "bf16 MFMA" + (" (E2M1 decoded to bf16 in LDS)" if cfg.wfmt else "")),
+           "tokens_per_s": round(cfg.T / sec, 1), "us_per_layer": round(sec * 1e6, 1), "tflops": round(tf, 2),
+           "mfma_bf16_frac": round(tf / BF16_PEAK_TFLOPS, 4)}
+    if cfg.wfmt:
+        rec["mfma_fp4_frac"] = round(tf / FP4_PEAK_TFLOPS, 4)
+    if mx:
+        rec["mx_two_term_frac"] = round(tf / MX_TWO_TERM_PEAK_TFLOPS, 4)
+    rec["gate_up_tflops"] = round(fl_gu / (stages["gate_up"] * 1e-6) / 1e12, 2)
+    rec["stages_us"] = {k: round(v, 1) for k, v in stages.items()}
+    return rec
 
 
 def n_copies_for(cfg, touched_bytes):
@@ -606,20 +629,20 @@ def secondary(steps, graph=False):
     import synth
     out = {}
     out["library_dense_gemm_bf16_tflops"] = library_gemm_tflops()
-    # prefill regimes: MFMA-bound
+    # prefill regimes: MFMA-bound.  MXFP4 runs on the MX kernel (the default
+    # tiled path) and, as "+dequant", on the bf16-decode kernel.
+    import mixture_experts_ffn_05_amd as moe
     for name in ("20b_prefill_zipf", "20b_mxfp4_prefill", "20b_mxfp4_prefill+packed"):
         layer = synth.make_layer(name.split("+")[0])
-        tm = Timed(layer, 1, name.endswith("+packed"))
-        sec = tm.run(max(3, steps // 10), 2)
-        stages = tm.stages(max(3, steps // 10), 1)
-        fl, fl_gu = layer_flops(layer.cfg)
-        peak = BF16_PEAK_TFLOPS  # the kernels issue bf16 MFMA (MXFP4 decoded to bf16 in LDS)
-        out[name] = {"tokens_per_s": round(layer.cfg.T / sec, 1), "us_per_layer": round(sec * 1e6, 1),
-                     "tflops": round(fl / sec / 1e12, 2), "mfma_bf16_frac": round(fl / sec / 1e12 / peak, 4),
-                     "mfma_fp4_frac": round(fl / sec / 1e12 / FP4_PEAK_TFLOPS, 4),
-                     "gate_up_tflops": round(fl_gu / (stages["gate_up"] * 1e-6) / 1e12, 2),
-                     "stages_us": {k: round(v, 1) for k, v in stages.items()}}
-        del tm, layer
+        mx = layer.cfg.wfmt != 0
+        for suffix, path in ([("", moe.MOE_PATH_AUTO), ("+dequant", moe.MOE_PATH_TILED_DEQUANT)] if mx
+                             else [("", moe.MOE_PATH_AUTO)]):
+            tm = Timed(layer, 1, name.endswith("+packed"), path=path)
+            sec = tm.run(max(3, steps // 10), 2)
+            stages = tm.stages(max(3, steps // 10), 1)
+            out[name + suffix] = prefill_record(layer.cfg, sec, stages, mx and not suffix)
+            del tm
+        del layer
     # decode regimes: HBM-bound
     # MXFP4 decode in the row-major order and in the packed order (moe_mxfp4_pack)
     for packed in (False, True):
@@ -737,14 +760,9 @@ def main():
         tm = Timed(layer, 1, packed, path=PATHS[args.path])
         sec = tm.run(args.steps, args.warmup)
         stages = tm.stages(args.steps, 1)
-        fl, fl_gu = layer_flops(layer.cfg)
+        mx = layer.cfg.wfmt != 0 and args.path in ("auto", "tiled", "tiled_mx")
         print(json.dumps({"workload": args.only, "path": args.path, "tokens": layer.cfg.T, "steps": args.steps,
-                          "us_per_layer": round(sec * 1e6, 1), "tokens_per_s": round(layer.cfg.T / sec, 1),
-                          "tflops": round(fl / sec / 1e12, 2),
-                          "mfma_bf16_frac": round(fl / sec / 1e12 / BF16_PEAK_TFLOPS, 4),
-                          "mfma_fp4_frac": round(fl / sec / 1e12 / FP4_PEAK_TFLOPS, 4),
-                          "gate_up_tflops": round(fl_gu / (stages["gate_up"] * 1e-6) / 1e12, 2),
-                          "stages_us": {k: round(v, 1) for k, v in stages.items()}}))
+                          **prefill_record(layer.cfg, sec, stages, mx)}))
         return
 
     layer = synth.make_layer("20b_decode")
