@@ -22,12 +22,13 @@
 // entry points have the gate/up epilogue split h itself).  mx_gemm_kernel is
 // the grouped GEMM, with the tile schedule and gate/up pairing of the bf16
 // tiled kernel (tile_sched.h):
-//   tile 256 weight rows x 256 tokens, 4 waves (one per SIMD) as 2 weight
-//   halves x 2 token halves, each wave 4 x 4 blocks of 32 x 32 in 256
+//   tile 256 weight rows x 256 tokens, 8 waves (two per SIMD) as 2 weight
+//   halves x 4 token quarters, each wave 4 x 2 blocks of 32 x 32 in 128
 //   accumulators; K advances in stages of 64 (two MX blocks: one MFMA per
-//   block pair and term) through a ring of 4 LDS buffers.
-// Token codes and scales go straight into LDS (global_load_lds) three stages
-// ahead.  Each tile row stays whole in LDS (its six 16-byte chunks of a stage
+//   block pair and term) through a ring of 4 LDS buffers.  With two waves per
+//   SIMD one wave's MFMAs run while the other waits on LDS or at a barrier.
+// Token codes and scales go straight into LDS (buffer loads to LDS) three
+// stages ahead.  Each tile row stays whole in LDS (its six 16-byte chunks of a stage
 // in rotated slots, see mx_chunk_slot), so one wave-wide load reads
 // consecutive 16-byte pieces of gathered rows and the fragment reads are free
 // of bank conflicts.  Weight codes and scales take registers two stages ahead
@@ -48,6 +49,7 @@ typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(32))) __bf16 bf16x32;
 typedef __attribute__((ext_vector_type(6))) unsigned int u32x6;
 typedef __attribute__((ext_vector_type(8))) unsigned int u32x8;
+typedef __attribute__((ext_vector_type(12))) unsigned int u32x12;
 
 // ------------------------------------------------------------------ split
 
@@ -144,16 +146,16 @@ hipError_t launch_mx_split(const uint16_t* in, int64_t rows, int K, uint8_t* cod
 
 // ------------------------------------------------------------------ GEMM
 
-constexpr int MX_THREADS = 256;
-constexpr int MX_WAVES = MX_THREADS / WAVE;  // 4: 2 weight halves x 2 token halves, one per SIMD
+constexpr int MX_THREADS = 512;
+constexpr int MX_WAVES = MX_THREADS / WAVE;  // 8: 2 weight halves x 4 token quarters, two per SIMD
 constexpr int MX_NBUF = 4;                   // LDS stages
 constexpr int MX_DIST = 3;                   // token loads run this many stages ahead
 constexpr int MX_WB = 4;                     // weight blocks per wave (128 rows)
-constexpr int MX_TB = 4;                     // token blocks per wave (128 tokens)
+constexpr int MX_TB = 2;                     // token blocks per wave (64 tokens)
 constexpr int MX_BAND = 4;                   // M-tiles per band of the tile order
 constexpr int MX_XCH = 2 * MX_CODE_BYTES / 16;  // 16-byte token code chunks per row and stage (6)
-constexpr int MX_XL = MX_XCH * GM_BT * 16 / 1024 / MX_WAVES;  // token code loads per wave per stage (6)
-constexpr int MX_SL = GM_BT * 4 / 256 / MX_WAVES;                // token scale loads per wave per stage (1)
+constexpr int MX_XL = MX_XCH * GM_BT * 16 / 1024 / MX_WAVES;  // token code loads per wave per stage (3)
+constexpr int MX_SW = GM_BT / WAVE;  // waves that load token scales, 64 rows x 4 B each (4)
 
 struct MxShared {
     uint8_t w[MX_NBUF][2][GM_BW][16];          // E2M1 codes: [block][row], 32 values per 16 B
@@ -206,7 +208,7 @@ __global__ __launch_bounds__(MX_THREADS, 1) void mx_gemm_kernel(FfnArgs a)
     const int tid = threadIdx.x, lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(tid / WAVE);
     const int r32 = lane & 31, kg = lane >> 5;
-    const int wt = wave % 2, ww = wave / 2;  // token half, weight half of this wave
+    const int wt = wave % 4, ww = wave / 4;  // token quarter, weight half of this wave
 
     // Activation row of tile row `row` (rows past the segment read a valid row;
     // their results are never stored).
@@ -217,56 +219,63 @@ __global__ __launch_bounds__(MX_THREADS, 1) void mx_gemm_kernel(FfnArgs a)
         else
             return (uint32_t)(s < seg1 ? s : 0);
     };
-    // ---- token codes and scales, straight into LDS.  Codes: the tile's 256
-    // rows x 6 chunk slots are filled in order, 1 KB (64 slots) per wave-wide
-    // load; load i of wave w covers slots 64 (w + 4 i) .. +63, and the lane of
-    // slot s fetches the chunk that belongs there: row s / 6, chunk j with
-    // mx_chunk_slot(row, j) = s % 6.  Consecutive lanes so read consecutive
-    // 16-byte pieces of the same gathered row.  Scales: wave w fills rows
-    // 64 w .. +63, lane l the 4 bytes (hi, lo of both blocks of the stage) of
-    // row 64 w + l.  Byte offsets stay below 2^31 (the split arrays of one
-    // call are checked against that on the host).
-    uint32_t xoff[MX_XL], soff[MX_SL];
+    // ---- token codes and scales, straight into LDS by buffer loads whose
+    // 32-bit lane offsets stay fixed for the tile (the stage's offset is a
+    // scalar).  Codes: the tile's 256 rows x 6 chunk slots are filled in order,
+    // 1 KB (64 slots) per wave-wide load; load i of wave w covers slots
+    // 64 (w + 8 i) .. +63, and the lane of slot s fetches the chunk that
+    // belongs there: row s / 6, chunk j with mx_chunk_slot(row, j) = s % 6.
+    // Consecutive lanes so read consecutive 16-byte pieces of the same gathered
+    // row.  Scales: waves 0-3, wave w filling rows 64 w .. +63, lane l the 4
+    // bytes (hi, lo of both blocks of the stage) of row 64 w + l.  Byte offsets
+    // stay below 2^31 (the split arrays of one call are checked against that
+    // on the host).
+    uint32_t xoff[MX_XL];
 #pragma unroll
     for (int i = 0; i < MX_XL; ++i) {
         const int slot = 64 * (wave + MX_WAVES * i) + lane, row = slot / MX_XCH, pos = slot % MX_XCH;
         const int j = (pos + ((row >> 3) & 1)) % MX_XCH;  // inverse of mx_chunk_slot
         xoff[i] = act_row(row) * (uint32_t)(nkb * MX_CODE_BYTES) + j * 16;
     }
-#pragma unroll
-    for (int j = 0; j < MX_SL; ++j) soff[j] = act_row(64 * (wave + MX_WAVES * j) + lane) * (uint32_t)(nkb * 2);
+    const uint32_t soff = act_row(WAVE * (wave % MX_SW) + lane) * (uint32_t)(nkb * 2);
+    const int arows = GATE_UP ? a.T : a.T * a.k;  // rows of the split activations
+    const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(a.a_codes), (short)0, arows * nkb * MX_CODE_BYTES, 0x00020000);
+    const __amdgpu_buffer_rsrc_t xsrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(a.a_scales), (short)0, arows * nkb * 2, 0x00020000);
 
-    typedef __attribute__((address_space(1))) const void* gptr_t;
     typedef __attribute__((address_space(3))) void* lptr_t;
     auto issue = [&](int st) {
         const int buf = st % MX_NBUF, kk = min(st, nstages - 1);
-        const uint8_t* cb = a.a_codes + (size_t)kk * 2 * MX_CODE_BYTES;
-        const uint8_t* sb = a.a_scales + (size_t)kk * 4;
 #pragma unroll
         for (int i = 0; i < MX_XL; ++i)
-            __builtin_amdgcn_global_load_lds((gptr_t)(cb + xoff[i]),
-                                             (lptr_t)(&sh.x[buf][0][0][0] + 1024 * (wave + MX_WAVES * i)), 16, 0, 0);
-#pragma unroll
-        for (int j = 0; j < MX_SL; ++j)
-            __builtin_amdgcn_global_load_lds((gptr_t)(sb + soff[j]), (lptr_t)&sh.xs[buf][64 * (wave + MX_WAVES * j)][0][0],
-                                             4, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (lptr_t)(&sh.x[buf][0][0][0] + 1024 * (wave + MX_WAVES * i)), 16,
+                                                     xoff[i], kk * 2 * MX_CODE_BYTES, 0, 0);
+        if (wave < MX_SW)  // uniform per wave
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xsrs, (lptr_t)&sh.xs[buf][WAVE * wave][0][0], 4, soff, kk * 4, 0, 0);
     };
 
-    // ---- weight codes and scales through registers: thread t takes the two
-    // 16-byte pieces (32 codes each) of tile row t at K-blocks 2 st and 2 st + 1,
-    // and their scale bytes.  Rows past the output width read the tile's first row.
-    long long qrow = gm_wrow<GATE_UP>(a, e, n0, NOUT, tid);
+    // ---- weight codes and scales through registers: thread t takes the
+    // 16-byte piece (32 codes) of tile row t % 256 at K-block 2 st + t / 256
+    // and its scale byte.  Rows past the output width read the tile's first
+    // row.  Offsets are 32-bit inside expert e's weights and scales (the host
+    // checks that one expert's weights stay below 2^31 bytes).
+    const int wr_ = tid % GM_BW, wb2 = tid / GM_BW;  // this thread's weight row and K-block of a stage
+    const int R = GATE_UP ? 2 * a.I : a.H;  // weight rows per expert
+    long long qrow = gm_wrow<GATE_UP>(a, e, n0, NOUT, wr_);
     if (qrow < 0) qrow = gm_wrow<GATE_UP>(a, e, 0, NOUT, 0);
-    const uint8_t* wbytes = static_cast<const uint8_t*>(a.w);
+    const int r = (int)(qrow - (long long)e * R);  // row inside the expert
+    const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(static_cast<const uint8_t*>(a.w) + (size_t)e * R * (K / 2)), (short)0, R * (K / 2),
+        0x00020000);
+    const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(a.w_scale + (size_t)e * R * nkb), (short)0, R * nkb, 0x00020000);
     // Packed MXFP4 order (moe_mxfp4_pack): the piece of K-block kb = 16c + b and
-    // its scale sit at pbase + 8192c + 64 g nb(c) + 64b and psbase + 512c + 32b,
-    // with slot 4g + t of item `it` fixed per thread.
-    long long pbase = 0, psbase = 0;
+    // its scale sit at wo + 8192c + 64 g nb(c) + 64b and so + 512c + 32b, with
+    // slot 4g + t of item `it` fixed per thread.  Row-major: wo + 16 kb, so + kb.
+    uint32_t wo, so;
     int pg = 0;
     if constexpr (PACKED) {
-        const int R = GATE_UP ? 2 * a.I : a.H;
-        const long long eq = qrow / R;
-        const int r = (int)(qrow % R);
         int it, q;
         if constexpr (GATE_UP) {
             const int n = r < a.I ? r : r - a.I;
@@ -277,34 +286,35 @@ __global__ __launch_bounds__(MX_THREADS, 1) void mx_gemm_kernel(FfnArgs a)
             q = r % 32;
         }
         pg = q / 4;
-        pbase = eq * R * (K / 2) + (long long)it * 512 * nkb + 16 * (q % 4);
-        psbase = eq * R * nkb + (long long)it * 32 * nkb + 8 * (q % 4) + pg;
+        wo = (uint32_t)it * 512u * nkb + 16u * (q % 4);
+        so = (uint32_t)it * 32u * nkb + 8u * (q % 4) + pg;
+    } else {
+        wo = (uint32_t)r * (uint32_t)(K / 2);
+        so = (uint32_t)r * (uint32_t)nkb;
     }
-    u32x4 wq[2][2];
-    uint32_t wsc[2][2];
+    u32x4 wq[2];
+    uint32_t wsc[2];
     auto fetch_w = [&](int set, int st) {
-#pragma unroll
-        for (int b2 = 0; b2 < 2; ++b2) {
-            const int kb = 2 * min(st, nstages - 1) + b2;
-            if constexpr (PACKED) {
-                const int c = kb >> 4, b = kb & 15, nb = min(16, nkb - 16 * c);
-                wq[set][b2] = *reinterpret_cast<const u32x4*>(wbytes + pbase + 8192ll * c + 64 * pg * nb + 64 * b);
-                wsc[set][b2] = a.w_scale[psbase + 512ll * c + 32 * b];
-            } else {
-                wq[set][b2] = *reinterpret_cast<const u32x4*>(wbytes + qrow * (K / 2) + kb * 16);
-                wsc[set][b2] = a.w_scale[qrow * nkb + kb];
-            }
+        const int kb = 2 * min(st, nstages - 1) + wb2;
+        uint32_t off, soff;
+        if constexpr (PACKED) {
+            const int c = kb >> 4, b = kb & 15, nb = min(16, nkb - 16 * c);
+            off = wo + 8192u * c + 64u * pg * nb + 64u * b;
+            soff = so + 512u * c + 32u * b;
+        } else {
+            off = wo + 16u * kb;
+            soff = so + kb;
         }
+        wq[set] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrs, off, 0, 0));
+        wsc[set] = __builtin_amdgcn_raw_buffer_load_b8(srs, soff, 0, 0);
     };
     auto store_w = [&](int set, int buf) {
-#pragma unroll
-        for (int b2 = 0; b2 < 2; ++b2) {
-            *reinterpret_cast<u32x4*>(&sh.w[buf][b2][tid][0]) = wq[set][b2];
-            sh.ws[buf][b2][tid] = (uint8_t)wsc[set][b2];
-        }
+        *reinterpret_cast<u32x4*>(&sh.w[buf][wb2][wr_][0]) = wq[set];
+        sh.ws[buf][wb2][wr_] = (uint8_t)wsc[set];
     };
-    // vector-memory operations per wave per stage: token loads, weight register loads
-    constexpr int L = MX_XL + MX_SL, QL = 4;
+    // vector-memory operations per wave per stage: token loads (codes, and
+    // scales in waves 0-3), weight register loads
+    constexpr int L = MX_XL + 1, QL = 2;
 
     f32x16 acc[MX_WB][MX_TB];
 #pragma unroll
@@ -313,69 +323,62 @@ __global__ __launch_bounds__(MX_THREADS, 1) void mx_gemm_kernel(FfnArgs a)
         for (int t = 0; t < MX_TB; ++t) acc[m][t] = f32x16{};
 
     // Operand fragments: lane l multiplies K-block kg = l / 32 of weight row
-    // 128 ww + 32 m + l % 32 and token row 128 wt + 32 t + l % 32.  A token
+    // 128 ww + 32 m + l % 32 and token row 64 wt + 32 t + l % 32.  A token
     // block's 48 code bytes sit in LDS as three 16-byte chunks c0 | c1 | c2
-    // (hi = c0 + the first half of c1, lo = the second half of c1 + c2): the
-    // hi term is read as c0, c1 into 8 consecutive registers (operand = the
-    // first 6), the lo term as c1, c2 (operand = the last 6), so each operand
-    // is a register range without copies.  Every fragment set has one copy,
-    // refilled right after its last use: the lo codes of stage st during its
-    // hi MFMAs, the hi codes and the weights of stage st+1 during its lo MFMAs
-    // (weights ordered by m, each weight block refilled once its four MFMAs
-    // are issued).
+    // (hi = c0 + the first half of c1, lo = the second half of c1 + c2) and
+    // are read into 12 consecutive registers: the hi operand is the first 6,
+    // the lo operand the last 6.  Every fragment set has one copy, refilled
+    // after its last use in the lo MFMAs: a token block's codes once its four
+    // lo MFMAs are issued, the weights during the last token block's.
     u32x4 fw[MX_WB];
     uint32_t fws[MX_WB], fxs[MX_TB];
-    u32x8 fhi[MX_TB], flo[MX_TB];
+    u32x12 fx[MX_TB];
     auto chunk = [&](int buf, int c, int t) {
-        const int row = 128 * wt + 32 * t + r32;
+        const int row = 32 * MX_TB * wt + 32 * t + r32;
         return *reinterpret_cast<const u32x4*>(&sh.x[buf][row][mx_chunk_slot(row, 3 * kg + c)][0]);
     };
-    auto cat = [](u32x4 a, u32x4 b) { return u32x8{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w}; };
     auto load_w = [&](int buf, int m) {
         const int row = 128 * ww + 32 * m + r32;
         fw[m] = *reinterpret_cast<const u32x4*>(&sh.w[buf][kg][row][0]);
         fws[m] = sh.ws[buf][kg][row];
     };
     auto load_hi = [&](int buf, int t) {
-        fhi[t] = cat(chunk(buf, 0, t), chunk(buf, 1, t));
-        fxs[t] = *reinterpret_cast<const uint16_t*>(&sh.xs[buf][128 * wt + 32 * t + r32][kg][0]);
+        const u32x4 c0 = chunk(buf, 0, t), c1 = chunk(buf, 1, t), c2 = chunk(buf, 2, t);
+        fx[t] = u32x12{c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w, c2.x, c2.y, c2.z, c2.w};
+        fxs[t] = *reinterpret_cast<const uint16_t*>(&sh.xs[buf][32 * MX_TB * wt + 32 * t + r32][kg][0]);
     };
-    auto load_lo = [&](int buf, int t) { flo[t] = cat(chunk(buf, 1, t), chunk(buf, 2, t)); };
-    auto first6 = [](const u32x8& v) { return __builtin_shufflevector(v, v, 0, 1, 2, 3, 4, 5); };
-    auto last6 = [](const u32x8& v) { return __builtin_shufflevector(v, v, 2, 3, 4, 5, 6, 7); };
-    // hi-term MFMAs of stage `buf`, token block by token block, each followed
-    // by the read of that block's lo codes
+    auto first6 = [](const u32x12& v) { return __builtin_shufflevector(v, v, 0, 1, 2, 3, 4, 5); };
+    auto last6 = [](const u32x12& v) { return __builtin_shufflevector(v, v, 6, 7, 8, 9, 10, 11); };
+    // hi-term MFMAs of stage `buf`
     auto phase_hi = [&](int buf) {
 #pragma unroll
         for (int t = 0; t < MX_TB; ++t) {
 #pragma unroll
             for (int m = 0; m < MX_WB; ++m)
-                acc[m][t] = mfma_mx<0>(fw[m], first6(fhi[t]), fws[m], fxs[t], acc[m][t]);
-            load_lo(buf, t);
+                acc[m][t] = mfma_mx<0>(fw[m], first6(fx[t]), fws[m], fxs[t], acc[m][t]);
         }
     };
-    // lo-term MFMAs, weight block by weight block, each followed by the read
-    // of that weight block for stage `nb`; then the hi codes of stage `nb`
+    // lo-term MFMAs, token block by token block, with the reads of stage `nb`'s
+    // fragments as their registers free up
     auto phase_lo = [&](int nb) {
         uint32_t xs_now[MX_TB];
 #pragma unroll
         for (int t = 0; t < MX_TB; ++t) xs_now[t] = fxs[t];
 #pragma unroll
-        for (int m = 0; m < MX_WB; ++m) {
-            const u32x4 w = fw[m];
-            const uint32_t ws = fws[m];
+        for (int t = 0; t < MX_TB; ++t) {
 #pragma unroll
-            for (int t = 0; t < MX_TB; ++t) acc[m][t] = mfma_mx<1>(w, last6(flo[t]), ws, xs_now[t], acc[m][t]);
-            load_w(nb, m);
+            for (int m = 0; m < MX_WB; ++m) {
+                acc[m][t] = mfma_mx<1>(fw[m], last6(fx[t]), fws[m], xs_now[t], acc[m][t]);
+                if (t == MX_TB - 1) load_w(nb, m);
+            }
+            load_hi(nb, t);
         }
-#pragma unroll
-        for (int t = 0; t < MX_TB; ++t) load_hi(nb, t);
     };
 
-    // Software pipeline, one K stage (64) per step.  Its 16 hi-term MFMAs are
+    // Software pipeline, one K stage (64) per step.  Its 8 hi-term MFMAs are
     // issued first and keep the matrix pipe busy while the wave stores the
     // next stage's weights, issues the weight loads of stage st+3 and waits
-    // at the barrier that publishes stage st+1; its 16 lo-term MFMAs then run
+    // at the barrier that publishes stage st+1; its 8 lo-term MFMAs then run
     // while stage st+1's fragments are read.  Token loads run MX_DIST stages
     // ahead, weight register loads two.  Every stage runs the same code: the
     // last one's reads of a next stage find the surplus loads (a re-read of
@@ -400,7 +403,10 @@ __global__ __launch_bounds__(MX_THREADS, 1) void mx_gemm_kernel(FfnArgs a)
         fetch_w(SET, st + 3);
         // outstanding after this wave's token loads of stage st+1: weight loads
         // of st+2, token loads of st+2, weight loads of st+3
-        vm_wait<L + 2 * QL>();
+        if (wave < MX_SW)
+            vm_wait<L + 2 * QL>();
+        else
+            vm_wait<L - 1 + 2 * QL>();
         lds_barrier();  // stage st+1 visible; the buffer of stage st-1 is free
         issue(st + MX_DIST);
         __builtin_amdgcn_sched_barrier(0);
@@ -417,7 +423,7 @@ __global__ __launch_bounds__(MX_THREADS, 1) void mx_gemm_kernel(FfnArgs a)
 
     // ---- epilogue: for each (m, t) the lane holds tile weight rows
     // 128ww + 32m + 8(r/4) + 4(lane/32) + r%4 (r = 0..15) of token
-    // 128wt + 32t + lane%32.
+    // 64wt + 32t + lane%32.
     if constexpr (GATE_UP && SPLIT_OUT) {
         // h goes out as the down GEMM's split activations (the bf16 h values
         // split as mx_split_kernel would split them).  Output columns
@@ -455,7 +461,7 @@ __global__ __launch_bounds__(MX_THREADS, 1) void mx_gemm_kernel(FfnArgs a)
             }
             u32x4 c[3];
             const uint32_t sb = mx_split_block(wv, c);
-            const int s = sbase + 128 * wt + 32 * t + r32;
+            const int s = sbase + 32 * MX_TB * wt + 32 * t + r32;
             if (s < seg1 && cols_in) {
                 const size_t blk = (size_t)s * nkb_out + kb;
                 u32x4* dst = reinterpret_cast<u32x4*>(a.out_codes + blk * MX_CODE_BYTES);
@@ -469,7 +475,7 @@ __global__ __launch_bounds__(MX_THREADS, 1) void mx_gemm_kernel(FfnArgs a)
     }
 #pragma unroll
     for (int t = 0; t < MX_TB; ++t) {
-        const int s = sbase + 128 * wt + 32 * t + r32;
+        const int s = sbase + 32 * MX_TB * wt + 32 * t + r32;
         if (s >= seg1) continue;
         if constexpr (GATE_UP) {
             // blocks m = 0, 1 are gate columns 64ww + 32m .., blocks m + 2 the matching up
@@ -507,7 +513,11 @@ __global__ __launch_bounds__(MX_THREADS, 1) void mx_gemm_kernel(FfnArgs a)
     }
 }
 
-bool mx_supported(int H, int I) { return H % 64 == 0 && I % 64 == 0; }
+bool mx_supported(int H, int I)
+{
+    // K stages of 64; one expert's weights addressed with 32-bit offsets
+    return H % 64 == 0 && I % 64 == 0 && (long long)I * H < (1ll << 31);
+}
 
 template <bool PACKED, bool GATE_UP, bool SPLIT_OUT>
 static hipError_t launch_mx(const FfnArgs& a, hipStream_t s)
