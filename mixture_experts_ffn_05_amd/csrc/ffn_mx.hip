@@ -208,7 +208,13 @@ __global__ __launch_bounds__(MX_THREADS, 1) void mx_gemm_kernel(FfnArgs a)
     const int tid = threadIdx.x, lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(tid / WAVE);
     const int r32 = lane & 31, kg = lane >> 5;
-    const int wt = wave % 4, ww = wave / 4;  // token quarter, weight half of this wave
+    // Weight half and token quarter of this wave.  Waves w and w + 4 share a
+    // SIMD and take token quarters two apart, so that in an expert's last,
+    // partly filled tile every SIMD keeps a wave with tokens: a wave whose
+    // quarter lies wholly past the segment skips its fragment reads and MFMAs
+    // (it still stages its share of the loads and meets every barrier).
+    const int ww = wave / 4, wt = (wave + 2 * ww) % 4;
+    const bool live = sbase + 32 * MX_TB * wt < seg1;
 
     // Activation row of tile row `row` (rows past the segment read a valid row;
     // their results are never stored).
@@ -390,15 +396,17 @@ __global__ __launch_bounds__(MX_THREADS, 1) void mx_gemm_kernel(FfnArgs a)
     fetch_w(0, 2);
     vm_wait<0>();
     lds_barrier();
+    if (live) {
 #pragma unroll
-    for (int m = 0; m < MX_WB; ++m) load_w(0, m);
+        for (int m = 0; m < MX_WB; ++m) load_w(0, m);
 #pragma unroll
-    for (int t = 0; t < MX_TB; ++t) load_hi(0, t);
+        for (int t = 0; t < MX_TB; ++t) load_hi(0, t);
+    }
     auto stage = [&](int st, auto set_c) {
         constexpr int SET = decltype(set_c)::value;
         const int buf = st % MX_NBUF, nb = (st + 1) % MX_NBUF;
         __builtin_amdgcn_sched_barrier(0);
-        phase_hi(buf);
+        if (live) phase_hi(buf);
         store_w(SET, nb);  // stage st+1, fetched two stages ago
         fetch_w(SET, st + 3);
         // outstanding after this wave's token loads of stage st+1: weight loads
@@ -410,7 +418,7 @@ __global__ __launch_bounds__(MX_THREADS, 1) void mx_gemm_kernel(FfnArgs a)
         lds_barrier();  // stage st+1 visible; the buffer of stage st-1 is free
         issue(st + MX_DIST);
         __builtin_amdgcn_sched_barrier(0);
-        phase_lo(nb);
+        if (live) phase_lo(nb);
     };
     int st = 0;
     for (; st + 1 < nstages; st += 2) {

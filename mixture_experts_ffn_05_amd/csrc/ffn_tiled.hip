@@ -139,7 +139,13 @@ __global__ __launch_bounds__(GM_THREADS, GM_WAVES / 4) void gemm_kernel(FfnArgs 
 
     const int tid = threadIdx.x, lane = lane_id(), wave = tid / WAVE;
     const int r32 = lane & 31, kg = lane >> 5;
-    const int wt = wave % 4, ww = wave / 4;  // token quarter, weight half of this wave
+    // Weight half and token quarter of this wave.  Waves w and w + 4 share a
+    // SIMD and take token quarters two apart, so that in an expert's last,
+    // partly filled tile every SIMD keeps a wave with tokens: a wave whose
+    // quarter lies wholly past the segment skips its fragment reads and MFMAs
+    // (it still stages its share of the loads and meets every barrier).
+    const int ww = wave / 4, wt = (wave + 2 * ww) % 4;
+    const bool live = sbase + 32 * GM_TB * wt < seg1;
 
     // ---- direct-to-LDS staging of bf16 tiles.  Wave w, load i covers tile
     // rows 16(w + 8i) .. +15; lane l lands in LDS slot l of that 1-KB span,
@@ -305,7 +311,7 @@ __global__ __launch_bounds__(GM_THREADS, GM_WAVES / 4) void gemm_kernel(FfnArgs 
     vm_wait<0>();
     lds_barrier();
     Frags f0, f1;
-    load_frags(0, 0, f0);
+    if (live) load_frags(0, 0, f0);
     // Stage st with st + 1 < nstages.  SET = (st + 1) & 1 is the MXFP4
     // register set holding stage st+1; a template constant, so that the two
     // sets stay in fixed registers.
@@ -313,9 +319,11 @@ __global__ __launch_bounds__(GM_THREADS, GM_WAVES / 4) void gemm_kernel(FfnArgs 
         constexpr int SET = decltype(set_c)::value;
         const int buf = st % GM_NBUF, nb = (st + 1) % GM_NBUF;
         __builtin_amdgcn_sched_barrier(0);
-        load_frags(buf, 1, f1);
-        mma(f0);
-        interleave();
+        if (live) {
+            load_frags(buf, 1, f1);
+            mma(f0);
+            interleave();
+        }
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (WFMT != 0) {
             store_q(SET, nb);             // stage st+1, fetched two stages ago
@@ -327,9 +335,11 @@ __global__ __launch_bounds__(GM_THREADS, GM_WAVES / 4) void gemm_kernel(FfnArgs 
         lds_barrier();  // stage st+1 visible; buffer of stage st-1 is free
         issue(st + GM_DIST);
         __builtin_amdgcn_sched_barrier(0);
-        load_frags(nb, 0, f0);
-        mma(f1);
-        interleave();
+        if (live) {
+            load_frags(nb, 0, f0);
+            mma(f1);
+            interleave();
+        }
     };
     int st = 0;
     for (; st + 2 < nstages; st += 2) {
@@ -338,10 +348,12 @@ __global__ __launch_bounds__(GM_THREADS, GM_WAVES / 4) void gemm_kernel(FfnArgs 
     }
     if (st + 1 < nstages) stage(st++, std::integral_constant<int, 1>{});
     __builtin_amdgcn_sched_barrier(0);
-    load_frags(st % GM_NBUF, 1, f1);
-    mma(f0);
-    interleave();
-    mma(f1);
+    if (live) {
+        load_frags(st % GM_NBUF, 1, f1);
+        mma(f0);
+        interleave();
+        mma(f1);
+    }
     mfma_drain();
     vm_wait<0>();  // the surplus loads past the last stage
     }
