@@ -29,6 +29,7 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 
 // Which expert and local tile a linear tile index belongs to.  Expert e owns
 // ceil(M_e / BT) * nt consecutive tiles.  One wave; returns -1 past the end.
+template <int BT = GM_BT>
 __device__ __forceinline__ int gm_locate(const int32_t* __restrict__ offsets, int E, int nt, int tile, int* local,
                                          int* mtiles)
 {
@@ -37,7 +38,7 @@ __device__ __forceinline__ int gm_locate(const int32_t* __restrict__ offsets, in
     for (int base = 0; base < E; base += WAVE) {
         const int e = base + lane;
         int mt = 0;
-        if (e < E) mt = (offsets[e + 1] - offsets[e] + GM_BT - 1) / GM_BT;
+        if (e < E) mt = (offsets[e + 1] - offsets[e] + BT - 1) / BT;
         const int n = mt * nt;
         const int excl = wave_excl_scan(n) + before;
         const uint64_t hm = ballot(n > 0 && tile >= excl && tile < excl + n);
@@ -52,12 +53,13 @@ __device__ __forceinline__ int gm_locate(const int32_t* __restrict__ offsets, in
     return -1;
 }
 
+template <int BT = GM_BT>
 __device__ __forceinline__ int gm_total_tiles(const int32_t* __restrict__ offsets, int E, int nt)
 {
     int n = 0;
     for (int base = 0; base < E; base += WAVE) {
         const int e = base + lane_id();
-        const int mt = e < E ? (offsets[e + 1] - offsets[e] + GM_BT - 1) / GM_BT : 0;
+        const int mt = e < E ? (offsets[e + 1] - offsets[e] + BT - 1) / BT : 0;
         n += wave_sum(mt);
     }
     return n * nt;

@@ -186,6 +186,36 @@ def make_x(cfg: LayerConfig, T: int | None = None) -> np.ndarray:
     return x
 
 
+# Experts of the near-tie router (near_tie_router): slot order by design.
+NEAR_TIE = {"A2": 17, "A1": 3, "B1": 5, "B2": 9, "C": 2}
+
+
+def near_tie_router(T: int, H: int, E: int, seed: int = 0):
+    """x [T][H] and a router [E][H] (bf16) whose logits are exact in fp64
+    whatever the summation order, with near ties at the top.  Every value is
+    a small integer times a power of two: x[:, 2:] integers in [-8, 8],
+    router entries integers in [-16, 16] / 256, so a logit is a multiple of
+    2^-20 below 2^11 in magnitude (31 bits).  Channel 0 of x is 1 and carries
+    a bias, channel 1 is 1 and carries a bump of +-2^-20.  Experts NEAR_TIE
+    share one random row: A1 and A2 have bias 512 and A2 the bump +2^-20, B1
+    and B2 are identical with bias 256, C has bias 256 and the bump -2^-20;
+    every other expert has its own random row and no bias (|logit| <= 127)."""
+    assert H >= 8 and E >= 18
+    rng = _rng(seed, 7)
+    x = rng.integers(-8, 9, size=(T, H)).astype(np.float32)
+    x[:, 0] = 1.0
+    x[:, 1] = 1.0
+    w = rng.integers(-16, 17, size=(E, H)).astype(np.float32) / 256.0
+    w[:, :2] = 0.0
+    common = rng.integers(-16, 17, size=H).astype(np.float32) / 256.0
+    for name, e in NEAR_TIE.items():
+        w[e, 2:] = common[2:]
+        w[e, 0] = 512.0 if name.startswith("A") else 256.0
+    w[NEAR_TIE["A2"], 1] = 2.0 ** -20
+    w[NEAR_TIE["C"], 1] = -(2.0 ** -20)
+    return bf16_from_f32(x), bf16_from_f32(w)
+
+
 def zipf_router_bias(cfg: LayerConfig) -> np.ndarray:
     """bf16 bias column ZIPF_GAIN * ln(p_e) for the router's last channel."""
     p = zipf_probs(cfg.E, cfg.zipf_s)

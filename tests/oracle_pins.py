@@ -535,6 +535,29 @@ def pin_route_nan_logits(o):
             assert not (idx == 1).any()
 
 
+def pin_route_near_ties(o):
+    """Near ties decided by 2^-20 in logits near 512 (relative 2^-29) and an
+    exact tie, on inputs whose logits are exact in fp64 in any order
+    (synth.near_tie_router): every token must take A2, A1, B1, B2 in that
+    order (the bump puts A2 before the lower-index A1; B1 and B2 tie exactly
+    and the lower index goes first; C, 2^-20 below them, is fifth), and the
+    logits must equal the exact sums computed in integers."""
+    for T, H, E in [(6, 64, 32), (3, 40, 128)]:
+        x, wr = synth.near_tie_router(T, H, E, seed=T)
+        lg, idx, w = o.route(x, wr, 4)
+        nt = synth.NEAR_TIE
+        want = [nt["A2"], nt["A1"], nt["B1"], nt["B2"]]
+        assert (idx == np.array(want)).all(), idx
+        # exact logits in units of 2^-20 (x integers, router entries multiples of 2^-20)
+        xi = np.rint(_f64(x)).astype(np.int64)
+        wi = np.rint(_f64(wr) * 2.0 ** 20).astype(np.int64)
+        exact = (xi @ wi.T).astype(np.float64) * 2.0 ** -20
+        assert np.array_equal(lg, exact)
+        _, idx5, _ = o.route(x, wr, 5)
+        assert (idx5[:, 4] == nt["C"]).all()
+        assert np.all(np.abs(w.sum(1) - 1.0) <= 1e-12)
+
+
 # --------------------------------------------------------------------------- permute pins
 
 
