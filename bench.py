@@ -625,14 +625,22 @@ def library_gemm_tflops(M: int = 32768, K: int = 2880, N: int = 5760, reps: int 
     return round(2.0 * M * K * N / sec / 1e12, 2)
 
 
+def progress(what: str):
+    """One line on stderr as each part of a long run starts (the JSON line
+    stays alone on stdout)."""
+    print(f"[bench] {what}", file=sys.stderr, flush=True)
+
+
 def secondary(steps, graph=False):
     import synth
     out = {}
+    progress("secondary: library dense GEMM")
     out["library_dense_gemm_bf16_tflops"] = library_gemm_tflops()
     # prefill regimes: MFMA-bound.  MXFP4 runs on the MX kernel (the default
     # tiled path) and, as "+dequant", on the bf16-decode kernel.
     import mixture_experts_ffn_05_amd as moe
     for name in ("20b_prefill_zipf", "20b_mxfp4_prefill", "20b_mxfp4_prefill+packed"):
+        progress(f"secondary: {name}")
         layer = synth.make_layer(name.split("+")[0])
         mx = layer.cfg.wfmt != 0
         for suffix, path in ([("", moe.MOE_PATH_AUTO), ("+dequant", moe.MOE_PATH_TILED_DEQUANT)] if mx
@@ -646,6 +654,7 @@ def secondary(steps, graph=False):
     # decode regimes: HBM-bound
     # MXFP4 decode in the row-major order and in the packed order (moe_mxfp4_pack)
     for packed in (False, True):
+        progress("secondary: 20b_mxfp4_decode" + ("+packed" if packed else ""))
         layer = synth.make_layer("20b_mxfp4_decode")
         tm, sec, stages, touched, total_b, gu_b = bench_decode(layer, steps, 10, graph, packed)
         rec = {"tokens_per_s": round(layer.cfg.T / sec, 1), "us_per_layer": round(sec * 1e6, 1),
@@ -656,6 +665,7 @@ def secondary(steps, graph=False):
             rec["gate_up_traffic_bytes"] = measured_traffic("gate_up_skinny4")
         out["20b_mxfp4_decode" + ("+packed" if packed else "")] = rec
         del tm, layer
+    progress("secondary: 120b sweep")
     base = synth.CONFIGS["120b_sweep"]
     w120 = synth.make_weights(base)
     sweep = {}
@@ -671,6 +681,7 @@ def secondary(steps, graph=False):
     del w120
     # the 120b shape with MXFP4 expert weights in the packed order (the pages' 120b is MXFP4)
     import torch
+    progress("secondary: 120b MXFP4 sweep")
     cfg4 = synth.CONFIGS["120b_mxfp4_sweep"]
     w4 = synth.make_weights(cfg4)
     sweep = {}
@@ -685,8 +696,10 @@ def secondary(steps, graph=False):
     del w4
     torch.cuda.empty_cache()
     out["120b_mxfp4_packed_sweep"] = sweep
+    progress("secondary: MXFP4 quantiser")
     out["mxfp4_quantize_20b_gate_up"] = bench_quantize(steps)
     out["backward_20b_prefill_zipf"] = bench_backward(steps)
+    progress("secondary: host-resident weights")
     out["host_weights_20b_mxfp4_decode"] = bench_host_weights("20b_mxfp4_decode")
     out["host_weights_20b_mxfp4_decode+packed"] = bench_host_weights("20b_mxfp4_decode", packed=True)
     return out
@@ -809,13 +822,14 @@ def main():
     rec["hbm_copy_gbs"] = copy_bandwidth()
     rec["roofline"]["frac_of_copy"] = round(achieved / rec["hbm_copy_gbs"], 4)
     if not args.no_secondary:
-        del tm
+        tm = None
         torch.cuda.empty_cache()
         rec["secondary"] = secondary(args.steps, args.graph)
     if not args.no_cpu:
+        progress("cpu baseline (the oracle on the host cores)")
         rec["cpu_baseline"] = cpu_baseline(layer)
     if args.copy_probe:
-        del tm
+        tm = None
         copy_probe()
     print(json.dumps(rec))
 
