@@ -625,6 +625,40 @@ def library_gemm_tflops(M: int = 32768, K: int = 2880, N: int = 5760, reps: int 
     return round(2.0 * M * K * N / sec / 1e12, 2)
 
 
+def library_mxfp8_gemm_tflops(M: int = 32768, K: int = 2944, N: int = 5760, reps: int = 10):
+    """The library's block-scaled GEMM on MX operands, as the reference point
+    for the MX kernel: torch's scaled matmul (hipBLASLt) with E4M3 x E4M3 and
+    one E8M0 scale per 32 along K, on random N(0, 1) data, at the grouped
+    gate/up's shape with K rounded up to the multiple of 128 it requires
+    (2880 -> 2944).  MXFP8 issues at the fp8 rate, the same as one product of
+    the MX kernel's two fp6 x fp4 terms.  This torch has no MXFP4 (E2M1 with
+    E8M0 per 32) scaled matmul.  Returns (TFLOP/s or None, note)."""
+    import torch
+    try:
+        g = torch.Generator(device="cuda")
+        g.manual_seed(12)
+        a = torch.randn((M, K), generator=g, device="cuda").to(torch.float8_e4m3fn)
+        b = torch.randn((N, K), generator=g, device="cuda").to(torch.float8_e4m3fn)
+        kb = (K // 32 + 3) // 4 * 4  # scale columns, padded as the library's blocked layout wants
+        sa = torch.full((M * kb,), 127, dtype=torch.uint8, device="cuda").view(torch.float8_e8m0fnu)
+        sb = torch.full((N * kb,), 127, dtype=torch.uint8, device="cuda").view(torch.float8_e8m0fnu)
+        fn = lambda: torch._scaled_mm(a, b.t(), sa, sb, out_dtype=torch.bfloat16)
+        for _ in range(3):
+            c = fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            c = fn()
+        e1.record()
+        torch.cuda.synchronize()
+        sec = e0.elapsed_time(e1) * 1e-3 / reps
+        del a, b, c, sa, sb
+        torch.cuda.empty_cache()
+        return round(2.0 * M * K * N / sec / 1e12, 2), f"[{M}x{K}]x[{K}x{N}] MXFP8, scales all 1"
+    except Exception as e:  # an older library without block-scaled MX support
+        return None, f"not available: {type(e).__name__}: {str(e)[:200]}"
+
+
 def progress(what: str):
     """One line on stderr as each part of a long run starts (the JSON line
     stays alone on stdout)."""
@@ -636,6 +670,7 @@ def secondary(steps, graph=False):
     out = {}
     progress("secondary: library dense GEMM")
     out["library_dense_gemm_bf16_tflops"] = library_gemm_tflops()
+    out["library_dense_gemm_mxfp8_tflops"], out["library_dense_gemm_mxfp8_note"] = library_mxfp8_gemm_tflops()
     # prefill regimes: MFMA-bound.  MXFP4 runs on the MX kernel (the default
     # tiled path) and, as "+dequant", on the bf16-decode kernel.
     import mixture_experts_ffn_05_amd as moe
