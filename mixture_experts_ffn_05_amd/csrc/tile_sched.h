@@ -17,7 +17,11 @@ namespace moe {
 
 constexpr int GM_BT = 256;    // tokens per tile
 constexpr int GM_BW = 256;    // weight rows per tile
-constexpr int GM_BAND = 4;    // M-tiles per band
+// M-tiles per band of the bf16 kernel's tile order.  (Measured on the 8192-token
+// Zipf prefill, interleaved repeats: 8 gives gate/up 1175 us and down 631 us
+// against 1199 and 641 us with 4; 12 and 16 the same as 8, 2 slower.  The MX
+// kernel, whose token tile is the larger operand, keeps bands of 4.)
+constexpr int GM_BAND = 8;
 
 // Workgroup barrier after this wave's LDS writes have completed.  It carries
 // no memory fence: the direct-to-LDS loads still in flight belong to later
