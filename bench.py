@@ -39,6 +39,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -261,6 +262,17 @@ class Timed:
     def touched_experts(self) -> int:
         off = self.g.offsets.cpu().numpy()
         return int(((off[1:] - off[:-1]) > 0).sum())
+
+
+def steady_steps(step_s: float, warm_s: float = 0.06, timed_s: float = 0.06, lo: int = 3, hi: int = 100):
+    """(timed steps, warmup steps) for a workload whose step takes about
+    step_s seconds: the untimed warmup lasts about warm_s, so that the GPU's
+    clock has settled under the load before the window opens, and the timed
+    window about timed_s (a few milliseconds of prefill work is too short for
+    either)."""
+    n = max(lo, min(hi, math.ceil(timed_s / step_s)))
+    w = max(2, min(hi, math.ceil(warm_s / step_s)))
+    return n, w
 
 
 def layer_bytes(cfg, touched: int):
@@ -539,10 +551,14 @@ def bench_backward(steps: int, name: str = "20b_prefill_zipf"):
     dgu = torch.empty((c.E, 2 * c.I, c.H), dtype=torch.float32, device="cuda")
     ddn = torch.empty((c.E, c.H, c.I), dtype=torch.float32, device="cuda")
     call = lambda: moe.moe_backward(d, x, wr, W, dy, dx, dwr, dgu, ddn, ws, nbytes)  # noqa: E731
-    for _ in range(2):
-        call()
+    call()
     torch.cuda.synchronize()
-    reps = max(3, steps // 20)
+    t0 = time.perf_counter()
+    call()
+    torch.cuda.synchronize()
+    reps, warm = steady_steps(time.perf_counter() - t0)
+    for _ in range(warm):
+        call()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(reps):
@@ -681,8 +697,9 @@ def secondary(steps, graph=False):
         for suffix, path in ([("", moe.MOE_PATH_AUTO), ("+dequant", moe.MOE_PATH_TILED_DEQUANT)] if mx
                              else [("", moe.MOE_PATH_AUTO)]):
             tm = Timed(layer, 1, name.endswith("+packed"), path=path)
-            sec = tm.run(max(3, steps // 10), 2)
-            stages = tm.stages(max(3, steps // 10), 1)
+            n, w = steady_steps(tm.run(1, 1))
+            sec = tm.run(n, w)
+            stages = tm.stages(n, w)
             out[name + suffix] = prefill_record(layer.cfg, sec, stages, mx and not suffix)
             del tm
         del layer
