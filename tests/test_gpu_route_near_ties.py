@@ -1,6 +1,6 @@
 """Near ties in the router on every top-k path of the GPU (per-token ranks for
-E <= 64 in the small-batch select+permute kernel and in the per-token
-selection kernel, arg-max rounds for E > 64, the selection fused into the
+E <= 64 in the small-batch select+permute kernel of up to 8 tokens and in
+the per-token selection kernel, arg-max rounds for E > 64, the selection fused into the
 fp64 matrix-core logits kernel from 1024 tokens).  The inputs
 (synth.near_tie_router) have logits that are exact in fp64 whatever the
 summation order, with two experts 2^-20 apart near 512 (relative 2^-29), an
@@ -20,7 +20,7 @@ from tests.gpu_layer import GpuLayer
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("T,E", [(16, 32), (16, 128), (300, 64), (2048, 32), (2048, 128)], ids=lambda v: str(v))
+@pytest.mark.parametrize("T,E", [(8, 32), (8, 128), (16, 32), (16, 128), (300, 64), (2048, 32), (2048, 128)], ids=lambda v: str(v))
 def test_near_ties(T, E):
     H, k, I = 256, 4, 64
     print(f"[near-tie] T={T} E={E}", flush=True)

@@ -1,12 +1,14 @@
-"""Small-batch routing: moe_forward runs selection and permutation as one
-workgroup after the logits kernel (select_permute_small), the stage entry
-points run moe_route (logits, then a per-token selection kernel) and
-moe_permute as separate launches.  Both must take the same decisions:
+"""Small-batch routing: for up to 8 tokens moe_forward runs selection and
+permutation as one workgroup after the logits kernel (select_permute_small),
+above that the parallel selection kernel and the permutation kernel; the
+stage entry points run moe_route (logits, then a per-token selection kernel)
+and moe_permute as separate launches.  Both must take the same decisions:
 routing indices and weights and the layer output identical bits, indices
 equal to the oracle's, output within 1e-2 * max|ref|.  Shapes cover one
-token, k = E, 64 pairs, 64 experts, one expert per token, exactly tied logits
-(duplicated router rows, resolved to the lower index) and the 20b MXFP4
-decode layer, with bf16 and packed MXFP4 experts."""
+token, k = E, 64 pairs in one wave (8 tokens x 8 experts), 64 experts, one
+expert per token, exactly tied logits (duplicated router rows, resolved to the
+lower index) and the 20b MXFP4 decode layer, on both sides of the 8-token
+switch, with bf16 and packed MXFP4 experts."""
 from __future__ import annotations
 
 import numpy as np
@@ -22,7 +24,8 @@ pytestmark = pytest.mark.gpu
 TOL = 1e-2
 
 SHAPES = [(16, 256, 32, 4, 128), (1, 128, 8, 2, 64), (5, 192, 64, 8, 128), (64, 128, 16, 1, 64),
-          (16, 64, 64, 4, 64), (3, 64, 3, 3, 64), (13, 128, 24, 4, 192)]
+          (16, 64, 64, 4, 64), (3, 64, 3, 3, 64), (13, 128, 24, 4, 192), (8, 64, 64, 8, 64),
+          (8, 128, 32, 4, 128), (9, 128, 32, 4, 128)]
 
 
 def _check(layer, tag):
@@ -58,10 +61,11 @@ def test_small_routing_matches_staged(shape, wfmt):
     _check(synth.make_layer(cfg), cfg.name)
 
 
-def test_small_routing_ties():
+@pytest.mark.parametrize("T", [16, 8])
+def test_small_routing_ties(T):
     """Router rows 2, 5 and 7 equal: their logits tie exactly for every token
     and go to the lower index."""
-    cfg = synth.LayerConfig("sr_ties", T=16, H=128, E=16, k=4, I=64, wfmt=1, seed=12)
+    cfg = synth.LayerConfig(f"sr_ties_T{T}", T=T, H=128, E=16, k=4, I=64, wfmt=1, seed=12)
     layer = synth.make_layer(cfg)
     wr = layer.w_router.copy()
     wr[5] = wr[2]
@@ -69,7 +73,7 @@ def test_small_routing_ties():
     _check(synth.Layer(cfg, layer.x, wr, layer.weights), cfg.name)
 
 
-@pytest.mark.parametrize("T", [16, 1])
+@pytest.mark.parametrize("T", [16, 8, 1])
 def test_small_routing_20b(T):
     cfg = synth.CONFIGS["20b_mxfp4_decode"].with_T(T)
     w = synth.make_weights(synth.CONFIGS["20b_mxfp4_decode"])
