@@ -85,6 +85,7 @@ __global__ __launch_bounds__(256) void router_logits_f64_kernel(int T, int H, in
 // cover the block's 32 products once, each exact in fp64.  A workgroup takes
 // two 16-expert tiles when E <= 32, else four.
 constexpr int RL_WAVES = 4;
+constexpr int RL_D = 3;  // 32-element blocks of H in flight per wave
 
 typedef __attribute__((ext_vector_type(4))) double f64x4;
 
@@ -122,34 +123,55 @@ __global__ __launch_bounds__(RL_WAVES * WAVE) void router_logits_mfma_kernel(int
 #pragma unroll
     for (int j = 0; j < RL_ET; ++j) acc[j] = f64x4{0, 0, 0, 0};
 
+    // Wave w takes blocks w, w + RL_WAVES, ...; RL_D of them are in flight in
+    // a ring of registers indexed by compile-time slots.  The loads are not
+    // conditional (a block index past the end reads the last block again, in
+    // bounds and unused), so no register is merged or copied between loop
+    // trips and the wait before a block's MFMAs covers only its own loads.
+    // A slot's operands are converted before its next block's loads are
+    // issued into it.
     const int nb = H / 32;  // H is a multiple of 32
-    int b = wave;
-    u32x4 xv = {0, 0, 0, 0}, wv[RL_ET];
+    u32x4 xv[RL_D], wv[RL_D][RL_ET];
+    auto load = [&](int sl, int b) {
+        const int bc = min(b, nb - 1);
+        xv[sl] = *reinterpret_cast<const u32x4*>(xr + 32 * bc);
 #pragma unroll
-    for (int j = 0; j < RL_ET; ++j) wv[j] = u32x4{0, 0, 0, 0};
-    if (b < nb) {
-        xv = *reinterpret_cast<const u32x4*>(xr + 32 * b);
+        for (int j = 0; j < RL_ET; ++j) wv[sl][j] = *reinterpret_cast<const u32x4*>(wrow[j] + 32 * bc);
+    };
 #pragma unroll
-        for (int j = 0; j < RL_ET; ++j) wv[j] = *reinterpret_cast<const u32x4*>(wrow[j] + 32 * b);
-    }
-    for (; b < nb; b += RL_WAVES) {
-        // this block's operands, then the next block's loads, then the MFMAs
-        double xd[8], wd[RL_ET][8];
-        bf16x8_to_f64(xv, xd);
+    for (int sl = 0; sl < RL_D; ++sl) load(sl, wave + RL_WAVES * sl);
+    int b0 = wave;
+    for (; b0 + RL_WAVES * (RL_D - 1) < nb; b0 += RL_WAVES * RL_D) {  // all RL_D slots hold blocks
 #pragma unroll
-        for (int j = 0; j < RL_ET; ++j) bf16x8_to_f64(wv[j], wd[j]);
-        const int bn = b + RL_WAVES;
-        if (bn < nb) {
-            xv = *reinterpret_cast<const u32x4*>(xr + 32 * bn);
+        for (int sl = 0; sl < RL_D; ++sl) {
+            double xd[8], wd[RL_ET][8];
+            bf16x8_to_f64(xv[sl], xd);
 #pragma unroll
-            for (int j = 0; j < RL_ET; ++j) wv[j] = *reinterpret_cast<const u32x4*>(wrow[j] + 32 * bn);
+            for (int j = 0; j < RL_ET; ++j) bf16x8_to_f64(wv[sl][j], wd[j]);
+            load(sl, b0 + RL_WAVES * (sl + RL_D));
+#pragma unroll
+            for (int s = 0; s < 8; ++s)
+#pragma unroll
+                for (int j = 0; j < RL_ET; ++j)
+                    acc[j] = __builtin_amdgcn_mfma_f64_16x16x4f64(xd[s], wd[j][s], acc[j], 0, 0, 0);
+            // keep the next slot's conversions (and so its wait) after these MFMAs
+            __builtin_amdgcn_sched_barrier(0);
         }
+    }
+#pragma unroll
+    for (int sl = 0; sl < RL_D - 1; ++sl) {  // the last blocks, already loaded
+        if (b0 + RL_WAVES * sl >= nb) break;  // uniform
+        double xd[8], wd[RL_ET][8];
+        bf16x8_to_f64(xv[sl], xd);
+#pragma unroll
+        for (int j = 0; j < RL_ET; ++j) bf16x8_to_f64(wv[sl][j], wd[j]);
 #pragma unroll
         for (int s = 0; s < 8; ++s)
 #pragma unroll
-            for (int j = 0; j < RL_ET; ++j) acc[j] = __builtin_amdgcn_mfma_f64_16x16x4f64(xd[s], wd[j][s], acc[j], 0, 0, 0);
-        if (bn >= nb) mfma_drain();  // accumulators are read right after the loop
+            for (int j = 0; j < RL_ET; ++j)
+                acc[j] = __builtin_amdgcn_mfma_f64_16x16x4f64(xd[s], wd[j][s], acc[j], 0, 0, 0);
     }
+    mfma_drain();  // accumulators are read right after the loop
     if (wave > 0) {
 #pragma unroll
         for (int j = 0; j < RL_ET; ++j) red[wave - 1][j][lane] = acc[j];
