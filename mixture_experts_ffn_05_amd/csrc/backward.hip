@@ -134,6 +134,89 @@ __global__ __launch_bounds__(WAVE) void pad_offsets_kernel(const int32_t* __rest
     if (lane == 0) padoff[E] = run;
 }
 
+// ------------------------------------------------------------------ router weight gradient
+// dWr[e] = sum over expert e's sorted rows i (token t_i) of dl_i * x[t_i], in
+// two passes that fix the order of every sum.  Pass 1: each expert segment is
+// cut into splits of RW_ROWS consecutive sorted rows (the splits of all
+// experts numbered in expert order, as locate_m_tile numbers M-tiles), and a
+// workgroup sums its split's rows for RW_COLS hidden columns in row order, in
+// fp32, into part[split][H].  Pass 2 adds an expert's splits in split order.
+// dl_i is the bf16 value router_bwd_kernel wrote to dlT.
+constexpr int RW_ROWS = 64;                 // sorted rows per split (one per lane of a wave)
+constexpr int RW_THREADS = 256;
+constexpr int RW_COLS = RW_THREADS * 4;     // hidden columns per workgroup, 4 per thread
+constexpr int RW_BATCH = 16;                // row loads in flight per thread
+
+__global__ __launch_bounds__(RW_THREADS) void router_wgrad_partial_kernel(
+    int H, int E, int k, const int32_t* __restrict__ offsets, const int32_t* __restrict__ padoff,
+    const int32_t* __restrict__ sorted_pairs, const uint16_t* __restrict__ dlT, const uint16_t* __restrict__ x,
+    float* __restrict__ part)
+{
+    int mt;
+    const int e = locate_m_tile(offsets, E, RW_ROWS, blockIdx.x, &mt);  // the same in every wave
+    if (e < 0) return;  // uniform: past the last split
+    const int r0 = mt * RW_ROWS;
+    const int n = min(RW_ROWS, offsets[e + 1] - offsets[e] - r0);
+    const int lane = lane_id();
+    int tok = 0;
+    float dl = 0.f;
+    if (lane < n) {
+        tok = sorted_pairs[offsets[e] + r0 + lane] / k;
+        dl = bf16_to_f32(dlT[padoff[e] + r0 + lane]);
+    }
+    const int h = blockIdx.y * RW_COLS + threadIdx.x * 4;  // H % 32 == 0: all 4 columns or none
+    const bool col_ok = h < H;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int i0 = 0; i0 < n; i0 += RW_BATCH) {
+        uint2 v[RW_BATCH];
+#pragma unroll
+        for (int i = 0; i < RW_BATCH; ++i) {
+            const int t = __builtin_amdgcn_readlane(tok, i0 + i);
+            v[i] = (col_ok && i0 + i < n) ? *reinterpret_cast<const uint2*>(x + (size_t)t * H + h) : uint2{0, 0};
+        }
+#pragma unroll
+        for (int i = 0; i < RW_BATCH; ++i) {
+            if (i0 + i < n) {  // uniform
+                const float d = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(dl), i0 + i));
+                acc[0] = fmaf(d, bf16_lo(v[i].x), acc[0]);
+                acc[1] = fmaf(d, bf16_hi(v[i].x), acc[1]);
+                acc[2] = fmaf(d, bf16_lo(v[i].y), acc[2]);
+                acc[3] = fmaf(d, bf16_hi(v[i].y), acc[3]);
+            }
+        }
+    }
+    if (col_ok) *reinterpret_cast<float4*>(part + (size_t)blockIdx.x * H + h) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+}
+
+// Pass 2: one thread per (expert, column); an expert without rows gets zeros.
+__global__ __launch_bounds__(RW_THREADS) void router_wgrad_reduce_kernel(int H, int E,
+                                                                         const int32_t* __restrict__ offsets,
+                                                                         const float* __restrict__ part,
+                                                                         float* __restrict__ dwr)
+{
+    __shared__ int first_split, n_splits;
+    const int e = blockIdx.y;
+    if (threadIdx.x < WAVE) {
+        const int lane = lane_id();
+        int before = 0;
+        for (int base = 0; base < e; base += WAVE) {
+            const int j = base + lane;
+            const int c = j < e ? (offsets[j + 1] - offsets[j] + RW_ROWS - 1) / RW_ROWS : 0;
+            before += wave_sum(c);
+        }
+        if (lane == 0) {
+            first_split = before;
+            n_splits = (offsets[e + 1] - offsets[e] + RW_ROWS - 1) / RW_ROWS;
+        }
+    }
+    __syncthreads();
+    const int h = blockIdx.x * RW_THREADS + threadIdx.x;
+    if (h >= H) return;
+    float sum = 0.f;
+    for (int j = 0; j < n_splits; ++j) sum += part[(size_t)(first_split + j) * H + h];
+    dwr[(size_t)e * H + h] = sum;
+}
+
 // ------------------------------------------------------------------ elementwise / reductions
 
 // Combine backward, one wave per sorted row s (pair p = sorted_pairs[s],
@@ -293,6 +376,26 @@ hipError_t launch_transpose_batched(const uint16_t* in, uint16_t* out, int nb, i
 }
 
 int backward_pad_rows(int P, int E) { return P + (TR_TILE - 1) * E; }
+
+// sum over experts of ceil(M_e / RW_ROWS) <= floor((P + (RW_ROWS - 1) E) / RW_ROWS)
+long long router_wgrad_splits(int P, int E) { return ((long long)P + (long long)(RW_ROWS - 1) * E) / RW_ROWS; }
+
+hipError_t launch_router_wgrad(int H, int E, int k, int P, const int32_t* offsets, const int32_t* padoff,
+                               const int32_t* sorted_pairs, const uint16_t* dlT, const uint16_t* x, float* part,
+                               float* dwr, hipStream_t s)
+{
+    const long long ns = router_wgrad_splits(P, E);
+    if (ns > 0) {
+        const dim3 grid((unsigned)ns, (H + RW_COLS - 1) / RW_COLS);
+        hipLaunchKernelGGL(router_wgrad_partial_kernel, grid, dim3(RW_THREADS), 0, s, H, E, k, offsets, padoff,
+                           sorted_pairs, dlT, x, part);
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    const dim3 grid2((H + RW_THREADS - 1) / RW_THREADS, E);
+    hipLaunchKernelGGL(router_wgrad_reduce_kernel, grid2, dim3(RW_THREADS), 0, s, H, E, offsets, part, dwr);
+    return hipGetLastError();
+}
 
 hipError_t launch_pad_offsets(const int32_t* offsets, int E, int32_t* padoff, uint16_t* dlT, hipStream_t s)
 {

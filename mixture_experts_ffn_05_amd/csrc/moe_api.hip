@@ -272,7 +272,7 @@ int do_down(const moe_dims& d, const void* h, const int32_t* off, const moe_expe
 // then the saved activations, the gradients in flight, the transposed
 // weights and the per-expert transposed segments (Ppad rows each).
 struct BwdLayout {
-    size_t gu, dO, dw, da, dgu, dxp, padoff, dlT, wdT, wguT, dOT, hT, dguT, xT, total;
+    size_t gu, dO, dw, da, dgu, dxp, padoff, dlT, wdT, wguT, dOT, hT, dguT, xT, rwp, total;
 };
 
 BwdLayout bwd_layout_for(const moe_dims& d)
@@ -300,6 +300,7 @@ BwdLayout bwd_layout_for(const moe_dims& d)
     L.hT = take(I * Ppad * 2);
     L.dguT = take(2 * I * Ppad * 2);
     L.xT = take(H * Ppad * 2);
+    L.rwp = take((size_t)moe::router_wgrad_splits((int)P, d.E) * H * sizeof(float));
     L.total = at;
     return L;
 }
@@ -420,7 +421,8 @@ int moe_backward(const moe_dims* dims, const void* x, const void* w_router, cons
     if ((rc = hip_status(moe::launch_transpose_segments(xb, H, true, off, padoff, sp, d.k, P, E, xT, s)))) return rc;
     if ((rc = hip_status(moe::launch_wgrad_tiled(dOT, hT, padoff, E, H, I, ddown, s)))) return rc;
     if ((rc = hip_status(moe::launch_wgrad_tiled(dguT, xT, padoff, E, 2 * I, H, dgate_up, s)))) return rc;
-    return hip_status(moe::launch_wgrad_tiled(dlT, xT, padoff, E, 1, H, dw_router, s));
+    return hip_status(moe::launch_router_wgrad(H, E, d.k, P, off, padoff, sp, dlT, xb, region<float>(ws, B.rwp),
+                                               dw_router, s));
 }
 
 int moe_workspace_size(const moe_dims* dims, size_t* bytes)

@@ -102,6 +102,12 @@ hipError_t launch_transpose_segments(const uint16_t* in, int C, bool gather, con
                                      uint16_t* out, hipStream_t s);
 hipError_t launch_wgrad_tiled(const uint16_t* A, const uint16_t* B, const int32_t* padoff, int E, int M, int N,
                               float* C, hipStream_t s);
+// Router weight gradient dwr [E][H] (fp32) from dlT and the token rows of x;
+// part holds router_wgrad_splits(P, E) rows of H floats.
+long long router_wgrad_splits(int P, int E);
+hipError_t launch_router_wgrad(int H, int E, int k, int P, const int32_t* offsets, const int32_t* padoff,
+                               const int32_t* sorted_pairs, const uint16_t* dlT, const uint16_t* x, float* part,
+                               float* dwr, hipStream_t s);
 hipError_t launch_combine_bwd(int P, int H, int k, const uint16_t* dy, const uint16_t* ys, const int32_t* sorted_pairs,
                               const float* topk_w, uint16_t* dO, float* dw, hipStream_t s);
 hipError_t launch_swiglu_bwd(int P, int I, const uint16_t* da, const uint16_t* gu, uint16_t* dgu, hipStream_t s);
