@@ -97,12 +97,16 @@ def test_exact_ties_go_to_lower_index():
         assert tied == sorted(tied)
 
 
-@pytest.mark.parametrize("shape", [(1037, 96, 5, 2), (1024, 64, 48, 4), (2050, 160, 200, 8), (4096, 2880, 32, 4)],
+@pytest.mark.parametrize("shape", [(1037, 96, 5, 2), (1024, 64, 48, 4), (2050, 160, 200, 8), (4096, 2880, 32, 4),
+                                   (1024, 384, 32, 4), (1100, 512, 128, 4)],
                          ids=lambda s: "T{}_H{}_E{}_k{}".format(*s))
 def test_route_many_tokens(shape):
     """The matrix-core logits path (from 1024 tokens on): token and expert
     counts off its 16-token / 64-expert tiles, plus exact ties from duplicated
-    router rows, against the oracle's route of every token."""
+    router rows, against the oracle's route of every token.  Each wave takes
+    every 4th 32-element block of H, three in flight: H = 64, 96, 160 leave it
+    1-2 blocks (no full ring), 384 exactly one ring, 512 one ring and one
+    block, 2880 seven rings and one or two blocks."""
     T, H, E, k = shape
     layer = _layer(T, H, E, k, 32)
     wr = layer.w_router.copy()
