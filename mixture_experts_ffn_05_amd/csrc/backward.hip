@@ -212,8 +212,17 @@ __global__ __launch_bounds__(RW_THREADS) void router_wgrad_reduce_kernel(int H, 
     __syncthreads();
     const int h = blockIdx.x * RW_THREADS + threadIdx.x;
     if (h >= H) return;
+    const float* col = part + (size_t)first_split * H + h;
     float sum = 0.f;
-    for (int j = 0; j < n_splits; ++j) sum += part[(size_t)(first_split + j) * H + h];
+    int j = 0;
+    for (; j + 8 <= n_splits; j += 8) {  // 8 loads in flight, added in split order
+        float v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[q] = col[(size_t)(j + q) * H];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) sum += v[q];
+    }
+    for (; j < n_splits; ++j) sum += col[(size_t)j * H];
     dwr[(size_t)e * H + h] = sum;
 }
 
