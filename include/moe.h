@@ -247,8 +247,10 @@ int moe_forward_noalloc(const moe_dims* dims, const void* x, const void* w_route
  * token through the softmax over the k selected logits,
  * dl_j = w_j (dw_j - sum_i w_i dw_i), dx += sum_j dl_j Wr[e_j],
  * dWr[e_j] += dl_j x.  The top-k selection itself is piecewise constant and
- * passes no gradient.  Products run on bf16 MFMA with fp32 accumulation;
- * intermediates (w dy, g and u, [dg; du], per-pair dx) are stored in bf16.
+ * passes no gradient.  The expert products run on bf16 MFMA with fp32
+ * accumulation, dWr on fp32 vector FMAs in a fixed order (sums over 64-row
+ * splits of each expert's sorted rows, then the splits in order);
+ * intermediates (w dy, g and u, [dg; du], per-pair dx, dl) are stored in bf16.
  * An expert that receives no token gets zero weight gradients; T = 0 writes
  * zeros to the three weight gradients and touches nothing else.
  * Workspace: moe_backward_workspace_size() bytes (it includes the forward's
