@@ -46,6 +46,9 @@ hipError_t launch_pad_offsets(const int32_t*, int, int32_t*, uint16_t*, hipStrea
 hipError_t launch_transpose_segments(const uint16_t*, int, bool, const int32_t*, const int32_t*, const int32_t*, int,
                                      int, int, uint16_t*, hipStream_t) { return count(); }
 hipError_t launch_wgrad_tiled(const uint16_t*, const uint16_t*, const int32_t*, int, int, int, float*, hipStream_t) { return count(); }
+long long router_wgrad_splits(int P, int E) { return ((long long)P + 63LL * E) / 64; }
+hipError_t launch_router_wgrad(int, int, int, int, const int32_t*, const int32_t*, const int32_t*, const uint16_t*,
+                               const uint16_t*, float*, float*, hipStream_t) { return count(); }
 hipError_t launch_combine_bwd(int, int, int, const uint16_t*, const uint16_t*, const int32_t*, const float*, uint16_t*,
                               float*, hipStream_t) { return count(); }
 hipError_t launch_swiglu_bwd(int, int, const uint16_t*, const uint16_t*, uint16_t*, hipStream_t) { return count(); }
