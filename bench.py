@@ -708,7 +708,9 @@ def secondary(steps, graph=False):
     for packed in (False, True):
         progress("secondary: 20b_mxfp4_decode" + ("+packed" if packed else ""))
         layer = synth.make_layer("20b_mxfp4_decode")
-        tm, sec, stages, touched, total_b, gu_b = bench_decode(layer, steps, 10, graph, packed)
+        # the headline's protocol: median of 5 windows of `steps` steps (one short window read 2-6% high
+        # right after the prefill lines)
+        tm, sec, stages, touched, total_b, gu_b = bench_decode(layer, steps, 20, graph, packed, repeats=5)
         rec = {"tokens_per_s": round(layer.cfg.T / sec, 1), "us_per_layer": round(sec * 1e6, 1),
                "touched_experts": touched, "hbm_frac": round(total_b / sec / 1e9 / HBM_PEAK_GBS, 4),
                "stages_us": {k: round(v, 1) for k, v in stages.items()}}
@@ -724,7 +726,7 @@ def secondary(steps, graph=False):
     for T in synth.SWEEP_120B:
         cfg = base.with_T(T)
         layer = synth.Layer(cfg, synth.make_x(cfg), synth.make_router(cfg), w120)
-        tm, sec, stages, touched, total_b, gu_b = bench_decode(layer, steps, 10, graph)
+        tm, sec, stages, touched, total_b, gu_b = bench_decode(layer, steps, 20, graph, repeats=3)
         sweep[str(T)] = {"us_per_layer": round(sec * 1e6, 1), "touched_experts": touched,
                          "hbm_frac": round(total_b / sec / 1e9 / HBM_PEAK_GBS, 4),
                          "gate_up_us": round(stages["gate_up"], 1)}
@@ -740,7 +742,7 @@ def secondary(steps, graph=False):
     for T in synth.SWEEP_120B:
         cfg = cfg4.with_T(T)
         layer = synth.Layer(cfg, synth.make_x(cfg), synth.make_router(cfg), w4)
-        tm, sec, stages, touched, total_b, gu_b = bench_decode(layer, steps, 10, graph, True)
+        tm, sec, stages, touched, total_b, gu_b = bench_decode(layer, steps, 20, graph, True, repeats=3)
         sweep[str(T)] = {"us_per_layer": round(sec * 1e6, 1), "touched_experts": touched,
                          "hbm_frac": round(total_b / sec / 1e9 / HBM_PEAK_GBS, 4),
                          "gate_up_us": round(stages["gate_up"], 1)}
@@ -814,7 +816,8 @@ def main():
         layer = synth.make_layer(args.only.split("+")[0])
         packed = args.only.endswith("+packed")
         if layer.cfg.T <= 64:  # decode: rotated weight copies, as in the decode lines of the full run
-            tm, sec, stages, touched, total_b, gu_b = bench_decode(layer, args.steps, args.warmup, False, packed)
+            tm, sec, stages, touched, total_b, gu_b = bench_decode(layer, args.steps, args.warmup, False, packed,
+                                                                   repeats=args.repeats)
             if args.copy_probe:
                 copy_probe()
             print(json.dumps({"workload": args.only, "tokens": layer.cfg.T, "steps": args.steps,
